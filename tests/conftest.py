@@ -1,0 +1,20 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size case, minutes on the host")
+
+
+@pytest.fixture(scope="session")
+def lib():
+    """The loaded C-ABI library (skips when the build is absent on CPU)."""
+    from fp8_quantized_linear_mxq_amd import _lib
+    return _lib.load()

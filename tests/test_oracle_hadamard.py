@@ -1,0 +1,89 @@
+"""Pins for oracle.hadamard: integer identities, a library routine
+(scipy.linalg.hadamard), norm preservation, involution and exact sums."""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import hadamard as oh
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 16, 32, 128])
+def test_sylvester_identities(n):
+    h = oh.sylvester(n)
+    assert np.array_equal(h @ h.T, n * np.eye(n, dtype=np.int64))
+    assert np.array_equal(h, h.T)
+    assert np.all(np.abs(h) == 1) and np.all(h[0] == 1) and np.all(h[:, 0] == 1)
+
+
+def test_matches_scipy():
+    scipy_linalg = pytest.importorskip("scipy.linalg")
+    for n in oh.SIZES:
+        assert np.array_equal(oh.sylvester(n), scipy_linalg.hadamard(n))
+    assert oh.sylvester(2).tolist() == [[1, 1], [1, -1]]
+
+
+def test_scale_factor_is_nearest():
+    for n in (16, 32, 128, 2, 8):
+        c = oh.scale_factor(n)
+        # c is within half an ulp of 1/sqrt(n): check c**2 * n against 1
+        exact = Fraction(c) ** 2 * n
+        ulp = Fraction(np.spacing(c))
+        lo, hi = (Fraction(c) - ulp / 2) ** 2 * n, (Fraction(c) + ulp / 2) ** 2 * n
+        assert lo <= 1 <= hi
+    assert oh.scale_factor(16) == 0.25
+
+
+@pytest.mark.parametrize("n", oh.SIZES)
+def test_unit_vectors_and_norm(n):
+    x = np.zeros((n, 2 * n), np.float32)
+    for j in range(n):
+        x[j, n + j] = 1.0
+    r = oh.rotate(x, n)
+    c = np.float32(oh.scale_factor(n))
+    assert np.all(r[:, :n] == 0)
+    assert np.array_equal(np.abs(r[:, n:]), np.full((n, n), c, np.float32))
+    assert np.array_equal(np.sign(r[:, n:]), oh.sylvester(n).astype(np.float32))
+    rng = np.random.default_rng(0)
+    y = rng.standard_normal((8, 4 * n)).astype(np.float32)
+    ry = oh.rotate(y, n)
+    for b in range(4):
+        nb = np.linalg.norm(y[:, b * n:(b + 1) * n].astype(np.float64), axis=1)
+        nr = np.linalg.norm(ry[:, b * n:(b + 1) * n].astype(np.float64), axis=1)
+        assert np.allclose(nr, nb, rtol=1e-6)
+    # rotating twice is the identity up to the two float32 roundings
+    assert np.allclose(oh.rotate(ry, n), y, rtol=0, atol=1e-5 * np.abs(y).max())
+
+
+def test_n16_single_rounding_exact():
+    rng = np.random.default_rng(1)
+    x = (rng.laplace(size=(4, 32)) * 100).astype(np.float32)
+    r = oh.rotate(x, 16)
+    h = oh.sylvester(16)
+    for i in range(4):
+        for b in range(2):
+            blk = [Fraction(float(v)) for v in x[i, 16 * b:16 * b + 16]]
+            for j in range(16):
+                s = sum(blk[t] * int(h[t, j]) for t in range(16)) / 4
+                assert r[i, 16 * b + j] == np.float32(float(s)) or \
+                    Fraction(float(r[i, 16 * b + j])) == Fraction(float(np.float32(s)))
+
+
+def test_exactness_guard():
+    x = np.zeros((1, 16), np.float32)
+    x[0, 0] = 1.0e20
+    x[0, 1] = 1.0e-20
+    with pytest.raises(ValueError):
+        oh.rotate(x, 16)
+    # the same range with bf16-width mantissas is exact
+    x2 = np.zeros((1, 16), np.float32)
+    x2[0, 0], x2[0, 1] = 2.0 ** 20, 2.0 ** -10
+    oh.rotate(x2, 16, mant_bits=7)
+
+
+def test_shape_errors():
+    with pytest.raises(ValueError):
+        oh.rotate(np.zeros((1, 24), np.float32), 16)
+    with pytest.raises(ValueError):
+        oh.rotate(np.zeros((1, 64), np.float32), 64)
