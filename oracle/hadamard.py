@@ -17,6 +17,10 @@ the readings are:
 * Rounding: the sum S = x_block @ H_n is exact (see below); c_n is the
   float64 nearest to 1/sqrt(n) (exactly 1/4 for n = 16); r is
   RN_fp32(RN_fp64(c_n * S)).  For n = 16 this is a single rounding.
+* An exactly-zero sum is the real number zero and rotates to +0.0 (the sign
+  an IEEE sum of signed zeros would give depends on the summation order,
+  which the rotation does not define); a nonzero sum that underflows keeps
+  its sign.
 
 S is computed in float64 and is exact when every partial sum fits in 53
 bits: with M the largest exponent of |x| in the block and L the smallest
@@ -95,5 +99,6 @@ def rotate(x: np.ndarray, n: int, mant_bits: int = 23) -> np.ndarray:
         raise ValueError("non-finite input is outside the contract")
     check_exact(xb, n, mant_bits)
     s = xb @ sylvester(n).astype(np.float64)          # exact (checked above)
+    s = np.where(s == 0.0, 0.0, s)                    # the real zero is +0
     r = (scale_factor(n) * s).astype(np.float32)
     return r.reshape(rows, k)

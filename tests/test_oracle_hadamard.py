@@ -87,3 +87,19 @@ def test_shape_errors():
         oh.rotate(np.zeros((1, 24), np.float32), 16)
     with pytest.raises(ValueError):
         oh.rotate(np.zeros((1, 64), np.float32), 64)
+
+
+def test_zero_sum_is_positive_zero():
+    # signed zeros and cancelling pairs: every exact-zero output is +0
+    x = np.zeros((2, 16), np.float32)
+    x[0, 1::2] = -0.0
+    x[1, 0], x[1, 1] = 3.0, 3.0          # outputs j with H[0,j] = -H[1,j] cancel
+    r = oh.rotate(x, 16)
+    zeros = r == 0
+    assert zeros.sum() == 16 + 8
+    assert not np.signbit(r[zeros]).any()
+    # an underflowing nonzero sum keeps its sign
+    t = np.zeros((1, 16), np.float32)
+    t[0, 0] = -2.0 ** -149
+    r = oh.rotate(t, 16)
+    assert np.all(r == 0) and np.all(np.signbit(r[0, :]) == (oh.sylvester(16)[0] > 0))
