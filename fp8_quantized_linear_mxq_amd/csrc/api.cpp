@@ -1,0 +1,305 @@
+// libmxq C ABI: argument validation and route dispatch (see include/mxq.h).
+//
+// Every check runs on the host before anything is enqueued, so an invalid
+// call returns an mxq_status without touching the device.  Valid calls are
+// asynchronous on the caller's stream; the library holds no state.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "kernels.h"
+#include "mxq.h"
+
+namespace {
+
+using namespace mxq;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int block_of(int fmt) { return fmt == MXQ_FMT_NVFP4 ? 16 : 32; }
+
+bool known_fmt(int fmt) { return fmt >= MXQ_FMT_MXFP4 && fmt <= MXQ_FMT_INT4; }
+
+int64_t code_bytes(int fmt, int64_t cols) { return fmt == MXQ_FMT_MXFP8 ? cols : cols / 2; }
+
+int64_t scale_bytes(int fmt, int64_t cols) {
+  const int64_t blocks = cols / block_of(fmt);
+  return fmt == MXQ_FMT_INT4 ? blocks * 4 : blocks;
+}
+
+mxq_status from_hip(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH; }
+
+// Validates a quantized operand's descriptor against its format.
+mxq_status check_qtensor(const mxq_qtensor* t) {
+  if (!t || !known_fmt(t->fmt) || t->reserved != 0 || t->rows < 0 || t->cols < 0)
+    return MXQ_ERR_INVALID_ARG;
+  if (t->cols % block_of(t->fmt)) return MXQ_ERR_SHAPE;
+  if (t->rows == 0 || t->cols == 0) return MXQ_OK;
+  if (!t->codes || !t->scales) return MXQ_ERR_INVALID_ARG;
+  if (t->fmt == MXQ_FMT_NVFP4 && !t->tensor_scale) return MXQ_ERR_INVALID_ARG;
+  if (t->ld_codes < code_bytes(t->fmt, t->cols) || t->ld_scales < scale_bytes(t->fmt, t->cols))
+    return MXQ_ERR_INVALID_ARG;
+  if (!aligned(t->codes, 16) || t->ld_codes % 16 || !aligned(t->scales, 4) || t->ld_scales % 4)
+    return MXQ_ERR_ALIGNMENT;
+  if (t->fmt == MXQ_FMT_INT4 && (!aligned(t->scales, 16) || t->ld_scales % 16))
+    return MXQ_ERR_ALIGNMENT;
+  return MXQ_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t mxq_version(void) { return MXQ_VERSION; }
+
+const char* mxq_status_string(int32_t status) {
+  switch (status) {
+    case MXQ_OK: return "ok";
+    case MXQ_ERR_INVALID_ARG: return "invalid argument";
+    case MXQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case MXQ_ERR_ALIGNMENT: return "misaligned pointer or leading dimension";
+    case MXQ_ERR_SHAPE: return "shape not a multiple of the block, tile or rotation size";
+    case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXQ_ERR_NO_DEVICE: return "no HIP device";
+    case MXQ_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+mxq_status mxq_storage(int32_t fmt, int64_t cols, int64_t* code_b, int64_t* scale_b) {
+  if (!known_fmt(fmt) || cols < 0 || !code_b || !scale_b) return MXQ_ERR_INVALID_ARG;
+  if (cols % block_of(fmt)) return MXQ_ERR_SHAPE;
+  *code_b = code_bytes(fmt, cols);
+  *scale_b = scale_bytes(fmt, cols);
+  return MXQ_OK;
+}
+
+int64_t mxq_workspace_size(int32_t op, int64_t rows, int64_t cols, int32_t fmt) {
+  if (rows < 0 || cols < 0) return -1;
+  switch (op) {
+    case MXQ_OP_QUANTIZE:
+      if (!known_fmt(fmt)) return -1;
+      return fmt == MXQ_FMT_NVFP4 ? (int64_t)kAmaxPartials * 4 : 0;
+    case MXQ_OP_GEMM:
+      return 0;
+    case MXQ_OP_SELECT:
+      // amax partials, the tensor scale, per-row SSE for up to 4 candidates
+      return (int64_t)kAmaxPartials * 4 + 64 + rows * 4 * 8;
+    default:
+      return -1;
+  }
+}
+
+int32_t mxq_act_format_for_step(const uint8_t* table, int32_t n_layers, int32_t n_buckets,
+                                int32_t layer, int32_t step, int32_t num_steps) {
+  if (!table || n_layers <= 0 || n_buckets <= 0 || layer < 0 || layer >= n_layers ||
+      num_steps <= 0 || step < 0 || step >= num_steps)
+    return -1;
+  int64_t bucket = ((int64_t)n_buckets * step) / num_steps;
+  if (bucket > n_buckets - 1) bucket = n_buckets - 1;
+  return table[(int64_t)layer * n_buckets + bucket];
+}
+
+mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        int32_t hadamard_n, const float* static_tensor_scale,
+                        const void* lr_l1t, int32_t lr_rank, float* lr_u, int64_t ld_u,
+                        mxq_qtensor* out, void* workspace, size_t ws_bytes, void* stream) {
+  if (!out || (dtype != MXQ_DT_F32 && dtype != MXQ_DT_BF16) || rows < 0 || cols < 0)
+    return MXQ_ERR_INVALID_ARG;
+  if (!known_fmt(out->fmt) || out->rows != rows || out->cols != cols) return MXQ_ERR_INVALID_ARG;
+  if (hadamard_n != 0 && hadamard_n != 16 && hadamard_n != 32 && hadamard_n != 128)
+    return MXQ_ERR_INVALID_ARG;
+  if (lr_rank < 0 || lr_rank > 128 || lr_rank % 16) return MXQ_ERR_INVALID_ARG;
+  if (cols % block_of(out->fmt) || (hadamard_n && cols % hadamard_n)) return MXQ_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  if (rows * (cols / 8) >= (int64_t)1 << 32) return MXQ_ERR_SHAPE;
+  if (!x || ldx < cols) return MXQ_ERR_INVALID_ARG;
+  const int esz = dtype == MXQ_DT_F32 ? 4 : 2;
+  if (!aligned(x, 16) || (ldx * esz) % 16) return MXQ_ERR_ALIGNMENT;
+  mxq_status st = check_qtensor(out);
+  if (st != MXQ_OK) return st;
+  if (lr_rank > 0) {
+    if (dtype != MXQ_DT_BF16) return MXQ_ERR_UNSUPPORTED;
+    if (!lr_l1t || !lr_u || ld_u < lr_rank) return MXQ_ERR_INVALID_ARG;
+    if (!aligned(lr_l1t, 16) || !aligned(lr_u, 16) || ld_u % 4) return MXQ_ERR_ALIGNMENT;
+  }
+  const bool dynamic_nv = out->fmt == MXQ_FMT_NVFP4 && !static_tensor_scale;
+  if (dynamic_nv && (!workspace || ws_bytes < (size_t)kAmaxPartials * 4)) return MXQ_ERR_WORKSPACE;
+
+  QuantizeArgs a;
+  a.x = x;
+  a.dtype = dtype;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ldx;
+  a.hadamard_n = hadamard_n;
+  a.fmt = out->fmt;
+  a.codes = static_cast<uint8_t*>(out->codes);
+  a.ld_codes = out->ld_codes;
+  a.scales = static_cast<uint8_t*>(out->scales);
+  a.ld_scales = out->ld_scales;
+  a.tensor_scale_out = out->tensor_scale;
+  a.static_tensor_scale = static_tensor_scale;
+  a.partials = static_cast<float*>(workspace);
+  hipError_t e = launch_quantize(a, as_stream(stream));
+  if (e != hipSuccess) return MXQ_ERR_LAUNCH;
+  if (lr_rank > 0) {
+    LoraDownArgs l;
+    l.x = static_cast<const uint16_t*>(x);
+    l.rows = rows;
+    l.cols = cols;
+    l.ldx = ldx;
+    l.l1t = static_cast<const uint16_t*>(lr_l1t);
+    l.rank = lr_rank;
+    l.u = lr_u;
+    l.ld_u = ld_u;
+    e = launch_lora_down(l, as_stream(stream));
+  }
+  return from_hip(e);
+}
+
+static mxq_status gemm_checks(const mxq_qtensor* a, const mxq_qtensor* w, const float* lr_u,
+                              int64_t ld_u, const void* lr_l2t, int32_t lr_rank, void* out,
+                              int64_t ld_out, int64_t n_out) {
+  mxq_status st = check_qtensor(a);
+  if (st != MXQ_OK) return st;
+  st = check_qtensor(w);
+  if (st != MXQ_OK) return st;
+  if (a->cols != w->cols) return MXQ_ERR_SHAPE;
+  if (n_out < 0 || lr_rank < 0 || lr_rank > 128 || lr_rank % 16) return MXQ_ERR_INVALID_ARG;
+  // activations: MXFP4, MXFP8 or NVFP4; weights: MXFP4, NVFP4 or INT4
+  if (a->fmt == MXQ_FMT_INT4 || w->fmt == MXQ_FMT_MXFP8) return MXQ_ERR_UNSUPPORTED;
+  if (a->rows == 0 || w->rows == 0 || n_out == 0) return MXQ_OK;
+  if (a->cols % 128) return MXQ_ERR_SHAPE;
+  if (a->rows > INT32_MAX || w->rows > INT32_MAX || a->cols > INT32_MAX || n_out > INT32_MAX)
+    return MXQ_ERR_SHAPE;
+  if (!out || ld_out < n_out) return MXQ_ERR_INVALID_ARG;
+  if (!aligned(out, 2)) return MXQ_ERR_ALIGNMENT;
+  if (lr_rank > 0) {
+    if (!lr_u || !lr_l2t || ld_u < lr_rank) return MXQ_ERR_INVALID_ARG;
+    if (!aligned(lr_u, 16) || ld_u % 4 || !aligned(lr_l2t, 16)) return MXQ_ERR_ALIGNMENT;
+  }
+  return MXQ_OK;
+}
+
+static hipError_t gemm_launch(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* col_map,
+                              const float* lr_u, int64_t ld_u, const void* lr_l2t,
+                              int32_t lr_rank, const void* bias, void* out, int64_t ld_out,
+                              int64_t n_out, hipStream_t s) {
+  GemmArgs g;
+  g.a_fmt = a->fmt;
+  g.w_fmt = w->fmt;
+  g.a_codes = static_cast<const uint8_t*>(a->codes);
+  g.lda = a->ld_codes;
+  g.a_scales = static_cast<const uint8_t*>(a->scales);
+  g.ld_as = a->ld_scales;
+  g.a_g = a->tensor_scale;
+  g.w_codes = static_cast<const uint8_t*>(w->codes);
+  g.ldw = w->ld_codes;
+  g.w_scales = static_cast<const uint8_t*>(w->scales);
+  g.ld_ws = w->ld_scales;
+  g.w_g = w->tensor_scale;
+  g.M = a->rows;
+  g.N = w->rows;
+  g.K = a->cols;
+  g.col_map = col_map;
+  g.u = lr_u;
+  g.ld_u = ld_u;
+  g.l2t = static_cast<const uint16_t*>(lr_l2t);
+  g.rank = lr_rank;
+  g.bias = static_cast<const uint16_t*>(bias);
+  g.out = static_cast<uint16_t*>(out);
+  g.ld_out = ld_out;
+  g.n_out = n_out;
+  // E2M1 x E2M1 is exact on the scaled MFMA; every other pair is dequantized
+  // exactly to 16-bit operands (E4M3 MFMA products are not summed to fp32
+  // accuracy on this hardware)
+  if (a->fmt == MXQ_FMT_MXFP4 && w->fmt == MXQ_FMT_MXFP4) return launch_gemm_mx(g, s);
+  return launch_gemm_dq(g, s);
+}
+
+mxq_status mxq_gemm(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* w_out_col,
+                    const float* lr_u, int64_t ld_u, const void* lr_l2t, int32_t lr_rank,
+                    const void* bias, void* out, int64_t ld_out, int64_t n_out,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  mxq_status st = gemm_checks(a, w, lr_u, ld_u, lr_l2t, lr_rank, out, ld_out, n_out);
+  if (st != MXQ_OK) return st;
+  if (a->rows == 0 || w->rows == 0 || n_out == 0) return MXQ_OK;
+  if (!w_out_col && w->rows > n_out) return MXQ_ERR_SHAPE;
+  return from_hip(gemm_launch(a, w, w_out_col, lr_u, ld_u, lr_l2t, lr_rank, bias, out, ld_out,
+                              n_out, as_stream(stream)));
+}
+
+mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int32_t n_groups,
+                          const int32_t* w_perm, const float* lr_u, int64_t ld_u,
+                          const void* lr_l2t, int32_t lr_rank, const void* bias, void* out,
+                          int64_t ld_out, int64_t n_out, void* workspace, size_t ws_bytes,
+                          void* stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  if (!w_groups || n_groups <= 0 || n_groups > 8) return MXQ_ERR_INVALID_ARG;
+  int64_t total = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    mxq_status st = gemm_checks(a, &w_groups[g], lr_u, ld_u, lr_l2t, lr_rank, out, ld_out, n_out);
+    if (st != MXQ_OK) return st;
+    total += w_groups[g].rows;
+  }
+  if (total > 0 && !w_perm) return MXQ_ERR_INVALID_ARG;
+  if (a->rows == 0 || n_out == 0) return MXQ_OK;
+  int64_t off = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    const mxq_qtensor* w = &w_groups[g];
+    if (w->rows > 0) {
+      hipError_t e = gemm_launch(a, w, w_perm + off, lr_u, ld_u, lr_l2t, lr_rank, bias, out,
+                                 ld_out, n_out, as_stream(stream));
+      if (e != hipSuccess) return MXQ_ERR_LAUNCH;
+    }
+    off += w->rows;
+  }
+  return MXQ_OK;
+}
+
+mxq_status mxq_select_format(const void* w, int32_t dtype, int64_t n, int64_t k, int64_t ldw,
+                             const int32_t* candidates, int32_t n_cand, uint8_t* choice_out,
+                             double* sse_out, int32_t* perm_out, int32_t* counts_out,
+                             float* g_out, void* workspace, size_t ws_bytes, void* stream) {
+  if ((dtype != MXQ_DT_F32 && dtype != MXQ_DT_BF16) || n < 0 || k < 0) return MXQ_ERR_INVALID_ARG;
+  if (!candidates || n_cand <= 0 || n_cand > 4) return MXQ_ERR_INVALID_ARG;
+  for (int i = 0; i < n_cand; ++i)
+    if (candidates[i] != MXQ_FMT_MXFP4 && candidates[i] != MXQ_FMT_NVFP4 &&
+        candidates[i] != MXQ_FMT_INT4)
+      return MXQ_ERR_UNSUPPORTED;
+  if (k % 32) return MXQ_ERR_SHAPE;
+  if (n == 0 || k == 0) return MXQ_OK;
+  if (n > INT32_MAX || n * (k / 8) >= (int64_t)1 << 32) return MXQ_ERR_SHAPE;
+  if (!w || !choice_out || ldw < k) return MXQ_ERR_INVALID_ARG;
+  const int esz = dtype == MXQ_DT_F32 ? 4 : 2;
+  if (!aligned(w, 16) || (ldw * esz) % 16) return MXQ_ERR_ALIGNMENT;
+  const int64_t need = mxq_workspace_size(MXQ_OP_SELECT, n, k, 0);
+  if (!workspace || ws_bytes < (size_t)need || !aligned(workspace, 16)) return MXQ_ERR_WORKSPACE;
+  SelectArgs a;
+  a.w = w;
+  a.dtype = dtype;
+  a.n = n;
+  a.k = k;
+  a.ldw = ldw;
+  for (int i = 0; i < 4; ++i) a.cand[i] = i < n_cand ? candidates[i] : 0;
+  a.n_cand = n_cand;
+  a.choice = choice_out;
+  a.sse = sse_out;
+  a.perm = perm_out;
+  a.counts = counts_out;
+  a.g_out = g_out;
+  char* ws = static_cast<char*>(workspace);
+  a.partials = reinterpret_cast<float*>(ws);
+  a.g_ws = reinterpret_cast<float*>(ws + (size_t)kAmaxPartials * 4);
+  a.sse_ws = reinterpret_cast<double*>(ws + (size_t)kAmaxPartials * 4 + 64);
+  return from_hip(launch_select(a, as_stream(stream)));
+}
+
+}  // extern "C"

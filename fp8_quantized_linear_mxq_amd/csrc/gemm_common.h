@@ -1,0 +1,122 @@
+// Pieces shared by the GEMM routes: parameters, tile order, LDS swizzle and
+// the epilogue (low-rank branch, bias, bf16 rounding, column map).
+#pragma once
+
+#include "device_common.h"
+
+namespace mxq {
+
+constexpr int BM = 128, BN = 128;
+constexpr int kThreads = 256;
+
+// XOR swizzle of 16-byte chunks within an LDS row of CH chunks: a wave's
+// 16-byte fragment reads (one row per lane) then hit distinct banks.
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH == 2) return (r >> 2) & 1;
+  else if constexpr (CH == 4) return ((r >> 2) ^ (r & 2)) & 3;
+  else return ((r >> 1) ^ ((r & 1) << 2)) & 7;
+}
+
+struct GemmP {
+  const uint8_t* a; int64_t lda; const uint8_t* as; int64_t ldas;
+  const uint8_t* w; int64_t ldw; const uint8_t* ws; int64_t ldws;
+  int M, N, K;
+  int tiles_m, tiles_n;
+  const int32_t* col_map;
+  const float* u; int64_t ld_u; const uint16_t* l2t; int rank;
+  const uint16_t* bias;
+  uint16_t* out; int64_t ld_out; int n_out;
+};
+
+__device__ __forceinline__ int remap_tile(int bid, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = bid & 7, y = bid >> 3;
+  return x < r ? x * (q + 1) + y : r * (q + 1) + (x - r) * q + y;
+}
+
+template <int OPSEL, int AF>
+__device__ __forceinline__ v16f mfma_scaled(const v8i& a, const v8i& b, const v16f& c, int sa,
+                                            int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, AF, 4, OPSEL, sa, OPSEL, sb);
+}
+
+// Epilogue shared with the other routes: add the low-rank branch on the
+// bf16 MFMA, bias, convert and store through the optional column map.
+template <bool LR>
+__device__ __forceinline__ void epilogue(const GemmP& p, v16f acc[2][2], float alpha,
+                                         int m0, int n0, int wm, int wn, int lane) {
+  const int l32 = lane & 31, half = lane >> 5;
+  int col_out[2];
+  bool col_ok[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + l32;
+    int c = -1;
+    if (n < p.N) c = p.col_map ? p.col_map[n] : n;
+    col_ok[j] = (c >= 0 && c < p.n_out);
+    col_out[j] = col_ok[j] ? c : 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] *= alpha;
+
+  if constexpr (LR) {
+    // u = u_hi + u_lo (bf16 halves, residual <= 2**-18 |u|) times L2 on the
+    // bf16 MFMA, K = rank for each half.
+    for (int t = 0; t < p.rank / 16; ++t) {
+      v8bf bfrag[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(
+            p.l2t + (int64_t)col_out[j] * p.rank + t * 16 + half * 8);
+        bfrag[j] = __builtin_bit_cast(v8bf, v);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        int row = m0 + wm * 64 + i * 32 + l32;
+        row = row < p.M ? row : p.M - 1;
+        const float* up = p.u + (int64_t)row * p.ld_u + t * 16 + half * 8;
+        const float4 f0 = *reinterpret_cast<const float4*>(up);
+        const float4 f1 = *reinterpret_cast<const float4*>(up + 4);
+        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hi[e] = f32_to_bf16_bits(f[e]);
+          lo[e] = f32_to_bf16_bits(f[e] - bf16_bits_to_f32(hi[e]));
+        }
+        uint4 hv, lv;
+        hv.x = hi[0] | (hi[1] << 16); hv.y = hi[2] | (hi[3] << 16);
+        hv.z = hi[4] | (hi[5] << 16); hv.w = hi[6] | (hi[7] << 16);
+        lv.x = lo[0] | (lo[1] << 16); lv.y = lo[2] | (lo[3] << 16);
+        lv.z = lo[4] | (lo[5] << 16); lv.w = lo[6] | (lo[7] << 16);
+        const v8bf ah = __builtin_bit_cast(v8bf, hv), al = __builtin_bit_cast(v8bf, lv);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bfrag[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bfrag[j], acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float b = (p.bias && col_ok[j]) ? bf16_bits_to_f32(p.bias[col_out[j]]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
+        if (row < p.M && col_ok[j])
+          p.out[(int64_t)row * p.ld_out + col_out[j]] =
+              (uint16_t)f32_to_bf16_bits(acc[i][j][q] + b);
+      }
+    }
+  }
+}
+
+}  // namespace mxq

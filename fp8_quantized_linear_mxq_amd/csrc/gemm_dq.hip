@@ -1,0 +1,393 @@
+// GEMM routes on exact 16-bit dequantization: every (activation, weight)
+// format pair except MXFP4 x MXFP4 (which runs on the scaled MFMA directly).
+//
+// Why dequantize: on gfx950 every MFMA that takes E4M3 operands keeps only
+// about 15 bits below the largest product of its dot product (measured: the
+// error reaches 2**-11 of the largest product), which cannot meet the layer's
+// 1e-5 * sum|a w| bound on heavy-tailed activations; the 16-bit MFMAs round
+// like fp32 and E2M1 x E2M1 on the scaled MFMA is exact.  Every code/scale
+// pair used here dequantizes exactly into a 16-bit float:
+//   E2M1 x E4M3 block scale (NVFP4)  <= 6 significant bits, in [2**-10, 2688]
+//   E4M3 x E8M0 (MXFP8), E2M1 x E8M0 (MXFP4)  <= 4 significant bits
+// so NVFP4 x NVFP4 runs on the fp16 MFMA (one hardware FP4->fp16 convert and
+// one packed fp16 multiply per two elements) and everything else on the bf16
+// MFMA (E8M0 exponents need bf16's range; the hardware converts apply an
+// E8M0 scale exactly).  NVFP4 tensor scales are applied in the epilogue.
+//
+// INT4 weight rows (Chameleon palette: symmetric int4 with an fp32 scale per
+// 32) cannot fold their arbitrary fp32 scale into a 16-bit operand, so each
+// 32-element block's partial sum comes from two bf16 MFMAs on the integer
+// codes (exact in bf16) and is scaled into an fp32 accumulator with one FMA
+// per output element.
+//
+// Tile 128x128, K-tile 64, 2x2 waves of 64x64, 32x32x16 MFMAs; operands are
+// dequantized while being stored to LDS, so each element is converted once
+// per workgroup rather than once per wave.
+#include "device_common.h"
+#include "gemm_common.h"
+#include "kernels.h"
+
+namespace mxq {
+namespace {
+
+constexpr int BK = 64;
+constexpr int RB = BK * 2;    // LDS bytes per row (16-bit elements)
+constexpr int CH = RB / 16;   // 16-byte chunks per LDS row
+constexpr int kSlabTiles = 32;
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+enum : int { K_NV = 0, K_MX8 = 1, K_MX4 = 2, K_I4 = 3 };
+
+struct DqParams {
+  GemmP g;
+  const float* a_gp;   // NVFP4 tensor scale of a
+  const float* w_gp;   // NVFP4 tensor scale of w
+};
+
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// 32 NVFP4 codes (16 bytes) with block scales s0 (elements 0-15) and s1
+// (16-31) -> 64 bytes of fp16 (FP16=true) or bf16 values.
+template <bool FP16>
+__device__ __forceinline__ void dq_fp4_nv(const uint4& c, float s0, float s1, uint4 out[4]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[16];
+  if constexpr (FP16) {
+    const v2h h0 = {(_Float16)s0, (_Float16)s0}, h1 = {(_Float16)s1, (_Float16)s1};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const v2h sc = (k < 2) ? h0 : h1;
+      o[4 * k + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[k], 1.0f, 0) * sc);
+      o[4 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[k], 1.0f, 1) * sc);
+      o[4 * k + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[k], 1.0f, 2) * sc);
+      o[4 * k + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[k], 1.0f, 3) * sc);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float sc = (k < 2) ? s0 : s1;
+      const v2f f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 0);
+      const v2f f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 1);
+      const v2f f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 2);
+      const v2f f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w[k], 1.0f, 3);
+      o[4 * k + 0] = pack_hi16(f0.x * sc, f0.y * sc);   // exact products, exact truncation
+      o[4 * k + 1] = pack_hi16(f1.x * sc, f1.y * sc);
+      o[4 * k + 2] = pack_hi16(f2.x * sc, f2.y * sc);
+      o[4 * k + 3] = pack_hi16(f3.x * sc, f3.y * sc);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+}
+
+// 32 MXFP4 codes with one E8M0 scale (a power of two) -> bf16.
+__device__ __forceinline__ void dq_fp4_mx(const uint4& c, float sc, uint4 out[4]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[16];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[4 * k + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[k], sc, 0));
+    o[4 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[k], sc, 1));
+    o[4 * k + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[k], sc, 2));
+    o[4 * k + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[k], sc, 3));
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+}
+
+// 32 int4 codes (two's complement nibbles) -> 32 bf16 integers.
+__device__ __forceinline__ void dq_int4(const uint4& c, uint4 out[4]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[16];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // sign-extend each nibble with an arithmetic shift
+      const float lo = (float)((int)(w[k] << (28 - 8 * j)) >> 28);
+      const float hi = (float)((int)(w[k] << (24 - 8 * j)) >> 28);
+      o[4 * k + j] = pack_hi16(lo, hi);
+    }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) out[k] = make_uint4(o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]);
+}
+
+// 16 E4M3 codes with one E8M0 scale -> bf16 (32 bytes).
+__device__ __forceinline__ void dq_fp8_mx(const uint4& c, float sc, uint4 out[2]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t o[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], sc, false));
+    o[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[k], sc, true));
+  }
+  out[0] = make_uint4(o[0], o[1], o[2], o[3]);
+  out[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+__device__ __forceinline__ float e8m0_f32(uint32_t code) {
+  return code == 0 ? 0x1p-127f : __uint_as_float(code << 23);
+}
+
+// Loader of one 4-bit operand (A or W): a 16-byte chunk of 32 codes per
+// thread per K-tile, plus its block scales.
+template <int KIND>
+struct Fp4Loader {
+  const uint8_t* code;
+  const uint8_t* scl;
+  bool ok;
+  int fc;
+  uint4 r;
+  uint32_t s;
+  __device__ void init(const uint8_t* base, int64_t ld, const uint8_t* sbase, int64_t lds, int row,
+                       int nrows, int fc_) {
+    fc = fc_;
+    ok = row < nrows;
+    code = base + (int64_t)(ok ? row : 0) * ld + fc * 16;
+    scl = sbase + (int64_t)(ok ? row : 0) * lds;
+  }
+  __device__ void load(int kt) {
+    r = ok ? *reinterpret_cast<const uint4*>(code + (int64_t)kt * 32) : make_uint4(0, 0, 0, 0);
+    if constexpr (KIND == K_NV) s = *reinterpret_cast<const uint32_t*>(scl + kt * 4);  // 4 x E4M3
+    else if constexpr (KIND == K_MX4) s = scl[kt * 2 + fc];                            // E8M0
+  }
+  template <bool FP16>
+  __device__ void convert(uint4 o[4]) const {
+    if constexpr (KIND == K_NV) {
+      dq_fp4_nv<FP16>(r, e4m3_value((s >> (16 * fc)) & 0xFFu), e4m3_value((s >> (16 * fc + 8)) & 0xFFu), o);
+    } else if constexpr (KIND == K_MX4) {
+      dq_fp4_mx(r, e8m0_f32(s), o);
+    } else {
+      dq_int4(r, o);
+    }
+  }
+};
+
+template <int AK, int WK, bool LR>
+__global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
+  const GemmP& p = dp.g;
+  constexpr bool FP16 = (AK == K_NV && WK == K_NV);
+  constexpr bool I4 = (WK == K_I4);
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * RB];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * RB];
+
+  const int tile = remap_tile(blockIdx.x, p.tiles_m * p.tiles_n);
+  const int m0 = (tile / p.tiles_n) * BM, n0 = (tile % p.tiles_n) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int KT = p.K / BK;
+
+  const int fr = tid >> 1, fc = tid & 1;      // 4-bit operands: row, 32-element chunk
+  Fp4Loader<WK> wl;
+  wl.init(p.w, p.ldw, p.ws, p.ldws, n0 + fr, p.N, fc);
+  Fp4Loader<AK == K_MX8 ? K_MX4 : AK> al;     // unused for E4M3 activations
+  if constexpr (AK != K_MX8) al.init(p.a, p.lda, p.as, p.ldas, m0 + fr, p.M, fc);
+  // E4M3 activations: two 16-byte chunks (16 elements each) per thread.
+  int ar8[2], ac8[2];
+  bool a_ok8[2];
+  const uint8_t* a_code8[2];
+  const uint8_t* a_scl8[2];
+  uint4 ra8[2];
+  uint32_t ras8[2];
+  if constexpr (AK == K_MX8) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = tid + i * kThreads;
+      ar8[i] = q >> 2;
+      ac8[i] = q & 3;
+      a_ok8[i] = (m0 + ar8[i]) < p.M;
+      a_code8[i] = p.a + (int64_t)(a_ok8[i] ? m0 + ar8[i] : 0) * p.lda + ac8[i] * 16;
+      a_scl8[i] = p.as + (int64_t)(a_ok8[i] ? m0 + ar8[i] : 0) * p.ldas;
+    }
+  }
+  // INT4 weights: this lane's output columns' fp32 block scales.
+  const float* sw_row[2];
+  float2 sw[2], nsw[2];
+  if constexpr (I4) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = n0 + wn * 64 + j * 32 + l32;
+      sw_row[j] = reinterpret_cast<const float*>(p.ws + (int64_t)(c < p.N ? c : p.N - 1) * p.ldws);
+    }
+  }
+
+  auto gload = [&](int kt) {
+    wl.load(kt);
+    if constexpr (AK == K_MX8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        ra8[i] = a_ok8[i] ? *reinterpret_cast<const uint4*>(a_code8[i] + (int64_t)kt * 64)
+                          : make_uint4(0, 0, 0, 0);
+        ras8[i] = a_scl8[i][kt * 2 + (ac8[i] >> 1)];
+      }
+    } else {
+      al.load(kt);
+    }
+    if constexpr (I4) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) nsw[j] = *reinterpret_cast<const float2*>(sw_row[j] + kt * 2);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint4 o[4];
+    wl.template convert<FP16>(o);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int c = fc * 4 + k;
+      *reinterpret_cast<uint4*>(&sB[buf][fr * RB + ((c ^ swz<CH>(fr)) * 16)]) = o[k];
+    }
+    if constexpr (AK == K_MX8) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint4 o2[2];
+        dq_fp8_mx(ra8[i], e8m0_f32(ras8[i]), o2);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int c = ac8[i] * 2 + k;
+          *reinterpret_cast<uint4*>(&sA[buf][ar8[i] * RB + ((c ^ swz<CH>(ar8[i])) * 16)]) = o2[k];
+        }
+      }
+    } else {
+      al.template convert<FP16>(o);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = fc * 4 + k;
+        *reinterpret_cast<uint4*>(&sA[buf][fr * RB + ((c ^ swz<CH>(fr)) * 16)]) = o[k];
+      }
+    }
+  };
+  auto mfma = [&](const uint4& a, const uint4& b, const v16f& c) -> v16f {
+    if constexpr (FP16)
+      return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a),
+                                                    __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a),
+                                                     __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+  };
+
+  v16f acc[2][2], tot[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      acc[i][j] = v16f{};
+      tot[i][j] = v16f{};
+    }
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if constexpr (I4) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sw[j] = nsw[j];
+    }
+    if (kt + 1 < KT) gload(kt + 1);
+    uint4 af[BK / 16][2], bf[BK / 16][2];
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = ks * 2 + half;
+        const int r = wm * 64 + i * 32 + l32;
+        af[ks][i] = *reinterpret_cast<const uint4*>(&sA[buf][r * RB + ((c ^ swz<CH>(r)) * 16)]);
+        const int rb = wn * 64 + i * 32 + l32;
+        bf[ks][i] = *reinterpret_cast<const uint4*>(&sB[buf][rb * RB + ((c ^ swz<CH>(rb)) * 16)]);
+      }
+    if constexpr (I4) {
+      // two 32-element blocks per K-tile: exact-ish block partials, then the
+      // fp32 block scale of each output column
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            v16f part = mfma(af[2 * b][i], bf[2 * b][j], v16f{});
+            part = mfma(af[2 * b + 1][i], bf[2 * b + 1][j], part);
+            const float s = b == 0 ? sw[j].x : sw[j].y;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = fmaf(part[q], s, acc[i][j][q]);
+          }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[ks][i], bf[ks][j], acc[i][j]);
+    }
+    if ((kt + 1) % kSlabTiles == 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          tot[i][j] += acc[i][j];
+          acc[i][j] = v16f{};
+        }
+    }
+    if (kt + 1 < KT) lstore(buf ^ 1);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] += tot[i][j];
+  float alpha = 1.0f;
+  if constexpr (AK == K_NV) alpha *= *dp.a_gp;
+  if constexpr (WK == K_NV) alpha *= *dp.w_gp;
+  epilogue<LR>(p, acc, alpha, m0, n0, wm, wn, lane);
+}
+
+template <int AK, int WK>
+hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
+  if (lr) gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
+  else gemm_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+template <int AK>
+hipError_t dispatch_w(int w_fmt, bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
+  switch (w_fmt) {
+    case FMT_NVFP4: return dispatch<AK, K_NV>(lr, grid, p, s);
+    case FMT_MXFP4: return dispatch<AK, K_MX4>(lr, grid, p, s);
+    case FMT_INT4: return dispatch<AK, K_I4>(lr, grid, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s) {
+  DqParams dp;
+  GemmP& p = dp.g;
+  p.a = a.a_codes; p.lda = a.lda; p.as = a.a_scales; p.ldas = a.ld_as;
+  p.w = a.w_codes; p.ldw = a.ldw; p.ws = a.w_scales; p.ldws = a.ld_ws;
+  p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K;
+  p.tiles_m = (int)((a.M + BM - 1) / BM);
+  p.tiles_n = (int)((a.N + BN - 1) / BN);
+  p.col_map = a.col_map;
+  p.u = a.u; p.ld_u = a.ld_u; p.l2t = a.l2t; p.rank = a.rank;
+  p.bias = a.bias;
+  p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
+  dp.a_gp = a.a_g;
+  dp.w_gp = a.w_g;
+  const dim3 grid(p.tiles_m * p.tiles_n);
+  const bool lr = a.rank > 0;
+  switch (a.a_fmt) {
+    case FMT_NVFP4: return dispatch_w<K_NV>(a.w_fmt, lr, grid, dp, s);
+    case FMT_MXFP8: return dispatch_w<K_MX8>(a.w_fmt, lr, grid, dp, s);
+    case FMT_MXFP4: return dispatch_w<K_MX4>(a.w_fmt, lr, grid, dp, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mxq

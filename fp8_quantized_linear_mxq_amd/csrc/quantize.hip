@@ -1,0 +1,521 @@
+// Block quantization kernels: MXFP4 / MXFP8 (E8M0 per 32), NVFP4 (E4M3 per 16
+// + fp32 tensor scale, two passes when the tensor scale is dynamic) and INT4
+// (fp32 per 32), each with an optional fused block-diagonal Hadamard rotation.
+//
+// Scale and rounding rules: "Bridging the Gap ... Microscaling FP4
+// Quantization" summary, the two reasons FP4 fails (MXFP4 power-of-two
+// scales, NVFP4 small groups with block and tensor scales); rotation: same
+// page, modification 3 (block-diagonal Hadamard rotation of activations).
+//
+// Work layout: the [rows, cols] input is walked as a flat sequence of 8-element
+// chunks (cols is a multiple of 32, so chunks never straddle rows and every
+// 16/32-element block is 2/4 consecutive lanes).  Each lane loads one 16-byte
+// (bf16) or 32-byte (fp32) chunk, so a wave reads 1-2 KB of contiguous memory
+// and writes its packed codes contiguously.  Block amax is a 2- or 4-lane
+// DPP reduction; the Hadamard butterfly runs in float64 registers for the
+// three in-lane stages and by lane exchange for the rest.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace mxq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 2;
+
+struct QParams {
+  const void* x;
+  int64_t ldx;
+  uint32_t cpr;     // 8-element chunks per row
+  uint32_t total;   // rows * cpr
+  uint8_t* codes;
+  int64_t ld_codes;
+  uint8_t* scales;
+  int64_t ld_scales;
+  float* g_out;
+  const float* g_static;
+  const float* partials;
+  int n_partials;
+};
+
+template <int HAD>
+__device__ constexpr double had_scale() {
+  // float64 nearest to 1/sqrt(n): 1/4, sqrt(2)/8, sqrt(2)/16
+  return HAD == 16 ? 0.25 : HAD == 32 ? 0x1.6a09e667f3bcdp-3 : 0x1.6a09e667f3bcdp-4;
+}
+
+template <int DT>
+__device__ __forceinline__ void load_chunk(const QParams& p, uint32_t row, uint32_t col,
+                                           bool active, float v[8]) {
+  if constexpr (DT == DT_BF16) {
+    uint4 q = make_uint4(0, 0, 0, 0);
+    if (active)
+      q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) +
+                                          (int64_t)row * p.ldx + col);
+    v[0] = bf16_bits_to_f32(q.x & 0xFFFFu); v[1] = bf16_bits_to_f32(q.x >> 16);
+    v[2] = bf16_bits_to_f32(q.y & 0xFFFFu); v[3] = bf16_bits_to_f32(q.y >> 16);
+    v[4] = bf16_bits_to_f32(q.z & 0xFFFFu); v[5] = bf16_bits_to_f32(q.z >> 16);
+    v[6] = bf16_bits_to_f32(q.w & 0xFFFFu); v[7] = bf16_bits_to_f32(q.w >> 16);
+  } else {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    if (active) {
+      const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p.x) +
+                                                        (int64_t)row * p.ldx + col);
+      a = q[0];
+      b = q[1];
+    }
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <int L>
+__device__ __forceinline__ void cross_stage(double h[8], int lane) {
+  const bool upper = (lane & L) != 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    double o = xor_lane_d<L>(h[i]);
+    h[i] = upper ? (o - h[i]) : (h[i] + o);
+  }
+}
+
+// r = RN_fp32(RN_fp64(c_n * S)) with S = (x_block @ H_n) summed exactly in
+// float64 by the Sylvester butterfly (element distances 1, 2, 4 in-lane, then
+// 8, 16, ... across lanes).
+template <int HAD>
+__device__ __forceinline__ void hadamard(float v[8], int lane) {
+  double h[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) h[i] = (double)v[i];
+#pragma unroll
+  for (int d = 1; d < 8; d <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i & d) continue;
+      double a = h[i], b = h[i + d];
+      h[i] = a + b;
+      h[i + d] = a - b;
+    }
+  }
+  if constexpr (HAD >= 16) cross_stage<1>(h, lane);
+  if constexpr (HAD >= 32) cross_stage<2>(h, lane);
+  if constexpr (HAD >= 64) cross_stage<4>(h, lane);
+  if constexpr (HAD >= 128) cross_stage<8>(h, lane);
+  constexpr double c = had_scale<HAD>();
+  // an exactly-zero sum is the real zero: + 0.0 turns -0 into +0 and leaves
+  // every nonzero value unchanged
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)(c * (h[i] + 0.0));
+}
+
+__device__ __forceinline__ float reduce_partials(const QParams& p) {
+  __shared__ float red[kThreads / 64];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < p.n_partials; i += kThreads) m = fmaxf(m, p.partials[i]);
+  m = group_max<64>(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+  return m;
+}
+
+template <int DT, int FMT, int HAD>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(QParams p) {
+  constexpr int LPB = (FMT == FMT_NVFP4) ? 2 : 4;  // lanes per quantization block
+  const int lane = threadIdx.x & 63;
+
+  float g = 0.f;
+  if constexpr (FMT == FMT_NVFP4) {
+    if (p.g_static) {
+      g = *p.g_static;
+    } else {
+      // tensor scale g = RN_fp32(A / 2688): the float64 quotient of two float32
+      // values rounds correctly to float32 (53 >= 2*24 + 2)
+      g = (float)((double)reduce_partials(p) / 2688.0);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && p.g_out) *p.g_out = g;
+  }
+
+  const uint32_t wave_global = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const uint32_t n_waves = (gridDim.x * kThreads) >> 6;
+  for (uint32_t base = wave_global * 64u * kUnroll; base < p.total;
+       base += n_waves * 64u * kUnroll) {
+    float v[kUnroll][8];
+    uint32_t rowv[kUnroll], colv[kUnroll];
+    bool act[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t c = base + u * 64u + lane;
+      act[u] = c < p.total;
+      rowv[u] = act[u] ? c / p.cpr : 0u;
+      colv[u] = act[u] ? (c - rowv[u] * p.cpr) * 8u : 0u;
+      load_chunk<DT>(p, rowv[u], colv[u], act[u], v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if constexpr (HAD > 0) hadamard<HAD>(v[u], lane);
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
+      const float amax = group_max<LPB>(m);
+
+      uint32_t code[8];
+      uint32_t sbyte = 0;
+      float sfloat = 0.f;
+      if constexpr (FMT == FMT_MXFP4) {
+        const int e = mx_exponent(amax, 2);
+        if (e >= -126) {
+          // hardware RNE convert of x / 2**e, saturating at 6 (exact: the
+          // scale is a normal power of two)
+          const float sc = ldexpf(1.0f, e);
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            const uint32_t b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[u][i], v[u][i + 1], sc, 0);
+            code[i] = b & 0xFu;
+            code[i + 1] = (b >> 4) & 0xFu;
+          }
+        } else {
+          float th[7];
+          e2m1_thresholds_pow2(e, th);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) code[i] = e2m1_encode(v[u][i], th);
+        }
+        sbyte = (uint32_t)(e + 127);
+      } else if constexpr (FMT == FMT_MXFP8) {
+        const int e = mx_exponent(amax, 8);
+        if (e >= -126) {
+          // hardware RNE convert of x / 2**e; it does not saturate above 464,
+          // so clamp to +-448 * 2**e first (every value there rounds to 448)
+          const float sc = ldexpf(1.0f, e), lim = 448.0f * sc;
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) {
+            const float x0 = fminf(fmaxf(v[u][i], -lim), lim);
+            const float x1 = fminf(fmaxf(v[u][i + 1], -lim), lim);
+            typedef short v2s __attribute__((ext_vector_type(2)));
+            const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x0, x1, sc, false);
+            const uint32_t b = __builtin_bit_cast(uint32_t, r);
+            code[i] = b & 0xFFu;
+            code[i + 1] = (b >> 8) & 0xFFu;
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) code[i] = e4m3_encode(ldexpf(v[u][i], -e));
+        }
+        sbyte = (uint32_t)(e + 127);
+      } else if constexpr (FMT == FMT_NVFP4) {
+        // s = RN_E4M3(amax / (6 g)) from the correctly rounded float64 quotient
+        sbyte = (g == 0.f) ? 0u : e4m3_encode_f64((double)amax / (6.0 * (double)g));
+        const double d = (double)e4m3_value(sbyte) * (double)g;   // exact
+        float th[7];
+        e2m1_thresholds_f64(d, th);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) code[i] = e2m1_encode(v[u][i], th);
+      } else {  // INT4: s = RN_fp32(amax / 7), q = clamp(RNE(x / s), -7, 7)
+        sfloat = (float)((double)amax / 7.0);
+        const double sd = (double)sfloat;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          double q = (sfloat == 0.f) ? 0.0 : rint((double)v[u][i] / sd);
+          q = fmin(7.0, fmax(-7.0, q));
+          code[i] = (uint32_t)((int)q) & 0xFu;
+        }
+      }
+
+      if (act[u]) {
+        const uint32_t row = rowv[u], col = colv[u];
+        if constexpr (FMT == FMT_MXFP8) {
+          uint2 w;
+          w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+          w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+          *reinterpret_cast<uint2*>(p.codes + (int64_t)row * p.ld_codes + col) = w;
+        } else {
+          uint32_t w = 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w |= code[i] << (4 * i);
+          *reinterpret_cast<uint32_t*>(p.codes + (int64_t)row * p.ld_codes + col / 2) = w;
+        }
+        if ((lane & (LPB - 1)) == 0) {
+          if constexpr (FMT == FMT_INT4) {
+            *reinterpret_cast<float*>(p.scales + (int64_t)row * p.ld_scales + (col / 32) * 4) =
+                sfloat;
+          } else {
+            const uint32_t blk = (FMT == FMT_NVFP4) ? col / 16 : col / 32;
+            p.scales[(int64_t)row * p.ld_scales + blk] = (uint8_t)sbyte;
+          }
+        }
+      }
+    }
+  }
+}
+
+// NVFP4 phase 1: per-workgroup max |r| over the (rotated) tensor.
+template <int DT, int HAD>
+__global__ __launch_bounds__(kThreads) void amax_kernel(QParams p, float* partials) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave_global = (blockIdx.x * kThreads + threadIdx.x) >> 6;
+  const uint32_t n_waves = (gridDim.x * kThreads) >> 6;
+  float m = 0.f;
+  for (uint32_t base = wave_global * 64u * kUnroll; base < p.total;
+       base += n_waves * 64u * kUnroll) {
+    float v[kUnroll][8];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      uint32_t c = base + u * 64u + lane;
+      bool act = c < p.total;
+      uint32_t row = act ? c / p.cpr : 0u;
+      uint32_t col = act ? (c - row * p.cpr) * 8u : 0u;
+      load_chunk<DT>(p, row, col, act, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if constexpr (HAD > 0) hadamard<HAD>(v[u], lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
+    }
+  }
+  __shared__ float red[kThreads / 64];
+  m = group_max<64>(m);
+  if (lane == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+    partials[blockIdx.x] = r;
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Per-output-channel format selection (Chameleon article, "the format is
+// chosen by the value distribution": try the available formats per output
+// channel, keep the least reconstruction error).  One workgroup per weight
+// row; every candidate's codes come from the same encoders as the quantize
+// kernel, and each squared error is exact in float64.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ double e2m1_mag(uint32_t c) {
+  const uint32_t m = c & 7u, e = m >> 1, man = m & 1u;
+  const double v = (e == 0) ? 0.5 * (double)man : ldexp(1.0 + 0.5 * (double)man, (int)e - 1);
+  return (c & 8u) ? -v : v;
+}
+
+struct SelParams {
+  QParams q;            // x = w, cpr, total (per row: cpr chunks)
+  int n_cand;
+  int cand[4];
+  double* sse;          // [n][n_cand]
+  uint8_t* choice;      // [n]
+};
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void select_kernel(SelParams sp) {
+  const QParams& p = sp.q;
+  const int lane = threadIdx.x & 63;
+  float g = (float)((double)reduce_partials(p) / 2688.0);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && p.g_out) *p.g_out = g;
+  const uint32_t row = blockIdx.x;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (uint32_t base = 0; base < p.cpr; base += kThreads) {
+    const uint32_t c = base + threadIdx.x;
+    const bool act = c < p.cpr;
+    float v[8];
+    load_chunk<DT>(p, row, act ? c * 8u : 0u, act, v);
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    const float a32 = group_max<4>(m), a16 = group_max<2>(m);
+    for (int ci = 0; ci < sp.n_cand; ++ci) {
+      double e2 = 0.0;
+      const int f = sp.cand[ci];
+      if (f == FMT_MXFP4) {
+        const int e = mx_exponent(a32, 2);
+        float th[7];
+        e2m1_thresholds_pow2(e, th);
+        const double sc = ldexp(1.0, e);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double d = (double)v[i] - e2m1_mag(e2m1_encode(v[i], th)) * sc;
+          e2 += d * d;
+        }
+      } else if (f == FMT_NVFP4) {
+        const uint32_t sb = (g == 0.f) ? 0u : e4m3_encode_f64((double)a16 / (6.0 * (double)g));
+        const double dsc = (double)e4m3_value(sb) * (double)g;
+        float th[7];
+        e2m1_thresholds_f64(dsc, th);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const double d = (double)v[i] - e2m1_mag(e2m1_encode(v[i], th)) * dsc;
+          e2 += d * d;
+        }
+      } else {  // INT4
+        const float s = (float)((double)a32 / 7.0);
+        const double sd = (double)s;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          double q = (s == 0.f) ? 0.0 : rint((double)v[i] / sd);
+          q = fmin(7.0, fmax(-7.0, q));
+          const double d = (double)v[i] - q * sd;
+          e2 += d * d;
+        }
+      }
+      acc[ci] += act ? e2 : 0.0;
+    }
+  }
+  __shared__ double red[4][kThreads / 64];
+  for (int ci = 0; ci < sp.n_cand; ++ci) {
+    double t = acc[ci];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+    if (lane == 0) red[ci][threadIdx.x >> 6] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int best = 0;
+    double best_v = 0.0;
+    for (int ci = 0; ci < sp.n_cand; ++ci) {
+      const double t = (red[ci][0] + red[ci][1]) + (red[ci][2] + red[ci][3]);
+      sp.sse[(int64_t)row * sp.n_cand + ci] = t;
+      if (ci == 0 || t < best_v) { best = ci; best_v = t; }
+    }
+    sp.choice[row] = (uint8_t)best;
+  }
+}
+
+// Stable grouping of rows by chosen candidate: counts and permutation.
+__global__ __launch_bounds__(256) void group_kernel(const uint8_t* choice, int n, int n_cand,
+                                                    int32_t* perm, int32_t* counts) {
+  __shared__ int cnt[256][4];
+  __shared__ int base[4];
+  const int t = threadIdx.x;
+  const int per = (n + 255) / 256;
+  const int lo = t * per, hi = min(n, lo + per);
+  int c[4] = {0, 0, 0, 0};
+  for (int r = lo; r < hi; ++r) c[choice[r]]++;
+  for (int k = 0; k < 4; ++k) cnt[t][k] = c[k];
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int k = 0; k < n_cand; ++k) {
+      base[k] = run;
+      int s = 0;
+      for (int i = 0; i < 256; ++i) { const int v = cnt[i][k]; cnt[i][k] = s; s += v; }
+      if (counts) counts[k] = s;
+      run += s;
+    }
+  }
+  __syncthreads();
+  if (perm) {
+    int pos[4];
+    for (int k = 0; k < 4; ++k) pos[k] = (k < n_cand) ? base[k] + cnt[t][k] : 0;
+    for (int r = lo; r < hi; ++r) perm[pos[choice[r]]++] = r;
+  }
+}
+
+template <int DT, int FMT>
+hipError_t dispatch_had(int had, dim3 grid, const QParams& p, hipStream_t s) {
+  switch (had) {
+    case 0: quantize_kernel<DT, FMT, 0><<<grid, kThreads, 0, s>>>(p); break;
+    case 16: quantize_kernel<DT, FMT, 16><<<grid, kThreads, 0, s>>>(p); break;
+    case 32: quantize_kernel<DT, FMT, 32><<<grid, kThreads, 0, s>>>(p); break;
+    case 128: quantize_kernel<DT, FMT, 128><<<grid, kThreads, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t dispatch_fmt(int fmt, int had, dim3 grid, const QParams& p, hipStream_t s) {
+  switch (fmt) {
+    case FMT_MXFP4: return dispatch_had<DT, FMT_MXFP4>(had, grid, p, s);
+    case FMT_MXFP8: return dispatch_had<DT, FMT_MXFP8>(had, grid, p, s);
+    case FMT_NVFP4: return dispatch_had<DT, FMT_NVFP4>(had, grid, p, s);
+    case FMT_INT4: return dispatch_had<DT, FMT_INT4>(had, grid, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t dispatch_amax(int had, dim3 grid, const QParams& p, float* partials, hipStream_t s) {
+  switch (had) {
+    case 0: amax_kernel<DT, 0><<<grid, kThreads, 0, s>>>(p, partials); break;
+    case 16: amax_kernel<DT, 16><<<grid, kThreads, 0, s>>>(p, partials); break;
+    case 32: amax_kernel<DT, 32><<<grid, kThreads, 0, s>>>(p, partials); break;
+    case 128: amax_kernel<DT, 128><<<grid, kThreads, 0, s>>>(p, partials); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
+  QParams p;
+  p.x = a.x;
+  p.ldx = a.ldx;
+  p.cpr = (uint32_t)(a.cols / 8);
+  p.total = (uint32_t)(a.rows * (a.cols / 8));
+  p.codes = a.codes;
+  p.ld_codes = a.ld_codes;
+  p.scales = a.scales;
+  p.ld_scales = a.ld_scales;
+  p.g_out = a.tensor_scale_out;
+  p.g_static = a.static_tensor_scale;
+  p.partials = a.partials;
+  p.n_partials = 0;
+
+  const uint32_t per_block = kThreads * kUnroll;
+  uint32_t blocks = (p.total + per_block - 1) / per_block;
+  if (blocks > 8192u) blocks = 8192u;
+  if (blocks == 0) return hipSuccess;
+
+  if (a.fmt == FMT_NVFP4 && a.static_tensor_scale == nullptr) {
+    uint32_t pb = blocks < (uint32_t)kAmaxPartials ? blocks : (uint32_t)kAmaxPartials;
+    p.n_partials = (int)pb;
+    hipError_t e = (a.dtype == DT_BF16)
+                       ? dispatch_amax<DT_BF16>(a.hadamard_n, dim3(pb), p, a.partials, s)
+                       : dispatch_amax<DT_F32>(a.hadamard_n, dim3(pb), p, a.partials, s);
+    if (e != hipSuccess) return e;
+  }
+  return (a.dtype == DT_BF16)
+             ? dispatch_fmt<DT_BF16>(a.fmt, a.hadamard_n, dim3(blocks), p, s)
+             : dispatch_fmt<DT_F32>(a.fmt, a.hadamard_n, dim3(blocks), p, s);
+}
+
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
+  SelParams sp;
+  QParams& p = sp.q;
+  p.x = a.w;
+  p.ldx = a.ldw;
+  p.cpr = (uint32_t)(a.k / 8);
+  p.total = (uint32_t)(a.n * (a.k / 8));
+  p.codes = nullptr; p.ld_codes = 0; p.scales = nullptr; p.ld_scales = 0;
+  p.g_out = a.g_out ? a.g_out : a.g_ws;
+  p.g_static = nullptr;
+  p.partials = a.partials;
+  if (a.n == 0) return hipSuccess;
+  const uint32_t per_block = kThreads * kUnroll;
+  uint32_t blocks = (p.total + per_block - 1) / per_block;
+  if (blocks > (uint32_t)kAmaxPartials) blocks = kAmaxPartials;
+  p.n_partials = (int)blocks;
+  hipError_t e = (a.dtype == DT_BF16) ? dispatch_amax<DT_BF16>(0, dim3(blocks), p, a.partials, s)
+                                      : dispatch_amax<DT_F32>(0, dim3(blocks), p, a.partials, s);
+  if (e != hipSuccess) return e;
+  sp.n_cand = a.n_cand;
+  for (int i = 0; i < 4; ++i) sp.cand[i] = i < a.n_cand ? a.cand[i] : 0;
+  sp.sse = a.sse ? a.sse : a.sse_ws;
+  sp.choice = a.choice;
+  if (a.dtype == DT_BF16) select_kernel<DT_BF16><<<dim3((unsigned)a.n), kThreads, 0, s>>>(sp);
+  else select_kernel<DT_F32><<<dim3((unsigned)a.n), kThreads, 0, s>>>(sp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.perm || a.counts) {
+    group_kernel<<<1, 256, 0, s>>>(a.choice, (int)a.n, a.n_cand, a.perm, a.counts);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace mxq

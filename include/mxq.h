@@ -1,0 +1,246 @@
+/*
+ * mxq.h -- C ABI of libmxq: block-scaled (microscaling) quantized linear
+ * layers on AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one path:
+ *   activations x [M, K] (fp32 or bf16)
+ *     -> optional block-diagonal Hadamard rotation along K       (mxq_quantize)
+ *     -> block quantization to MXFP4 / MXFP8 / NVFP4 (or INT4)   (mxq_quantize)
+ *     -> block-scaled GEMM against pre-quantized 4-bit weights,
+ *        fp32 accumulation, optional rank-r bf16 branch, bf16 out (mxq_gemm)
+ *   plus the weight-side per-output-channel format choice        (mxq_select_format)
+ *   and the timestep-bucket activation-format lookup             (mxq_act_format_for_step)
+ *
+ * Sources (pages the method is described on, cited by title and section):
+ *  - "Bridging the Gap Between Promise and Performance for Microscaling FP4
+ *    Quantization" (summary page): MXFP4 uses power-of-two block scales,
+ *    NVFP4 small groups with block and tensor scales (the two reasons FP4
+ *    fails); activations are rotated at inference by block-diagonal
+ *    Hadamard rotations (modification 3).
+ *  - Nunchaku / SVDQuant article, "main explanation": 4-bit weights and
+ *    activations (W4A4) plus a 16-bit low-rank branch.
+ *  - Chameleon format-selection article, "the format is chosen by the value
+ *    distribution": per-output-channel weight format by least reconstruction
+ *    error, activation format read from a table per timestep interval (ten
+ *    intervals), MXFP8 forced for concatenated-feature convolutions; "hardware
+ *    support" paragraph: channel-mixed formats need a grouped GEMM.
+ *
+ * Formats (OCP microscaling / OCP FP8 / NVFP4 definitions; the pages give no
+ * bit layouts):
+ *   MXFP4  E2M1 elements, one E8M0 scale per 32 elements along K
+ *   MXFP8  E4M3 elements, one E8M0 scale per 32
+ *   NVFP4  E2M1 elements, one E4M3 scale per 16, one fp32 tensor scale g
+ *   INT4   symmetric two's-complement int4, one fp32 scale per 32 (weights)
+ * Rounding: nearest, ties to even, saturating at the largest finite value,
+ * decided on the exact real quotient.  Scale rules:
+ *   MX     e = clamp(floor(log2 amax) - emax_elem, -127, 127), code e + 127,
+ *          emax_elem = 2 (E2M1) or 8 (E4M3); amax = 0 gives code 0.
+ *   NVFP4  g = RN_fp32(A / 2688), A = tensor amax; s = RN_E4M3(amax / (6 g)).
+ *   INT4   s = RN_fp32(amax / 7); q = clamp(RNE(x / s), -7, 7).
+ *
+ * Storage (all device memory, row-major, K contiguous):
+ *   codes   4-bit formats: [rows][K/2] bytes, element 2i in the low nibble
+ *           of byte i; MXFP8: [rows][K] bytes.
+ *   scales  MX: [rows][K/32] E8M0 bytes; NVFP4: [rows][K/16] E4M3 bytes;
+ *           INT4: [rows][K/32] fp32.
+ *   tensor_scale  NVFP4 only: one fp32 in device memory.
+ * Weights, like nn.Linear, are stored [out][in] with the reduction index
+ * contiguous: W [N][K], the low-rank factors as L1^T [r][K] and L2^T [N][r].
+ *
+ * Conventions for every entry point:
+ *  - Ownership: the caller allocates and owns every buffer (inputs, outputs,
+ *    workspace).  The library never allocates, frees or synchronizes.
+ *  - Streams: work is enqueued on `stream` (a hipStream_t passed as void*;
+ *    NULL is the default stream) and the call returns without waiting.
+ *  - Errors: invalid arguments are reported synchronously, before any work
+ *    is enqueued, as an mxq_status; a failed launch returns MXQ_ERR_LAUNCH.
+ *    Faults inside kernels surface at the caller's next synchronization.
+ *    No C++ exception crosses this interface.
+ *  - NaN or Inf inputs are outside the contract.
+ *  - The library keeps no state; calls on distinct streams are independent.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_VERSION 1
+
+typedef enum mxq_status {
+  MXQ_OK = 0,
+  MXQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, unknown enum      */
+  MXQ_ERR_UNSUPPORTED = 2, /* valid but unimplemented combination            */
+  MXQ_ERR_ALIGNMENT = 3,   /* pointer or leading dimension misaligned        */
+  MXQ_ERR_SHAPE = 4,       /* K not a multiple of the block / tile / rotation*/
+  MXQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
+  MXQ_ERR_NO_DEVICE = 6,   /* no HIP device available                        */
+  MXQ_ERR_LAUNCH = 7       /* kernel launch failed                           */
+} mxq_status;
+
+typedef enum mxq_format {
+  MXQ_FMT_MXFP4 = 1,
+  MXQ_FMT_MXFP8 = 2,
+  MXQ_FMT_NVFP4 = 3,
+  MXQ_FMT_INT4 = 4
+} mxq_format;
+
+typedef enum mxq_dtype { MXQ_DT_F32 = 1, MXQ_DT_BF16 = 2 } mxq_dtype;
+
+/* A quantized [rows, cols] tensor (cols = K, the reduction axis). */
+typedef struct mxq_qtensor {
+  int32_t fmt;           /* mxq_format                                      */
+  int32_t reserved;      /* must be 0                                       */
+  int64_t rows;
+  int64_t cols;
+  void* codes;           /* device; 16-byte aligned                         */
+  int64_t ld_codes;      /* bytes between rows; multiple of 16              */
+  void* scales;          /* device; 4-byte aligned                          */
+  int64_t ld_scales;     /* bytes between rows; multiple of 4               */
+  float* tensor_scale;   /* NVFP4: device pointer to g; otherwise NULL      */
+} mxq_qtensor;
+
+/*
+ * mxq_quantize -- rotate (optional) and block-quantize a [rows, cols] tensor.
+ *
+ * Computes the scale and element rules above (Microscaling FP4 summary, the
+ * two reasons FP4 fails) on r = x, or on r = x H_bd when hadamard_n > 0
+ * (same summary, modification 3): H_bd is block-diagonal along K with
+ * n-point Sylvester blocks scaled by 1/sqrt(n); the block sums are exact and
+ * r = RN_fp32(RN_fp64(c_n * S)) with c_n the float64 nearest 1/sqrt(n).
+ * The sums are exact when each n-block's inputs span at most 53 - log2(n) - 1
+ * bits between the top bit of the largest and the last mantissa bit of the
+ * smallest nonzero element (always true for bf16 inputs within 2**38).
+ *
+ *  x           device, dtype elements, row stride ldx (elements, >= cols);
+ *              16-byte aligned, ldx * sizeof(dtype) a multiple of 16.
+ *  dtype       MXQ_DT_F32 or MXQ_DT_BF16.
+ *  hadamard_n  0 (none), 16, 32 or 128; must divide cols.
+ *  static_tensor_scale  NVFP4 only: device pointer to a caller-chosen g
+ *              (then block scales saturate at 448), or NULL for the dynamic
+ *              g computed from this tensor (two passes over x).
+ *  lr_l1t, lr_rank, lr_u, ld_u  optional fused low-rank down projection of
+ *              the SVDQuant branch (Nunchaku article, main explanation):
+ *              u = x L1 on the unrotated bf16 input, with L1^T [lr_rank][cols]
+ *              bf16 (row stride cols) and u [rows][ld_u] fp32 out.
+ *              lr_rank is 0 (off) or a multiple of 16 up to 128; bf16 x only.
+ *  out         out->fmt, codes, scales, ld_* and (NVFP4) tensor_scale set by
+ *              the caller; rows/cols must equal rows/cols.  For NVFP4 the
+ *              tensor scale used is written to *out->tensor_scale.
+ *  workspace   device scratch of mxq_workspace_size(MXQ_OP_QUANTIZE, ...)
+ *              bytes (only dynamic NVFP4 needs any).
+ * Returns MXQ_ERR_SHAPE when cols is not a multiple of the block (32, or 16
+ * for NVFP4) or of hadamard_n.  rows == 0 is a no-op.
+ */
+mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                        int64_t ldx, int32_t hadamard_n,
+                        const float* static_tensor_scale,
+                        const void* lr_l1t, int32_t lr_rank, float* lr_u, int64_t ld_u,
+                        mxq_qtensor* out, void* workspace, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * mxq_gemm -- y = RN_bf16(alpha * Q(a) Q(w)^T + u L2 + bias) for one weight
+ * format (Nunchaku article, main explanation: 4-bit GEMM plus the 16-bit
+ * low-rank branch added in the same output).
+ *
+ *  a           quantized activations [M, K]: MXFP4, MXFP8 or NVFP4.
+ *  w           quantized weights [N, K]: MXFP4, NVFP4 or INT4.  Every pair
+ *              is supported: MXFP4 x MXFP4 on the scaled MFMA; the others
+ *              dequantize exactly to fp16 (NVFP4 x NVFP4) or bf16 operands;
+ *              INT4 rows sum each 32-block and apply its fp32 scale.
+ *  alpha       the product of the NVFP4 tensor scales of a and w that are
+ *              NVFP4 (read from their tensor_scale pointers on the device).
+ *  w_out_col   optional device int32[N]: weight row n writes output column
+ *              w_out_col[n] (the grouped mixed-format layout); NULL = n.
+ *              Entries outside [0, n_out) are skipped.
+ *  lr_u, ld_u, lr_l2t, lr_rank  optional low-rank branch: u [M][ld_u] fp32
+ *              from mxq_quantize, L2^T [n_out][lr_rank] bf16 indexed by the
+ *              output column; lr_rank 0 = off, else a multiple of 16 <= 128.
+ *  bias        optional device bf16 [n_out], indexed by output column.
+ *  out         device bf16 [M][ld_out], n_out columns; 4-byte aligned.
+ * Requirements: a->cols == w->cols == K, K a multiple of 128.
+ * M or N of 0 is a no-op.  Accumulation is fp32; long K is summed in slabs.
+ */
+mxq_status mxq_gemm(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* w_out_col,
+                    const float* lr_u, int64_t ld_u, const void* lr_l2t, int32_t lr_rank,
+                    const void* bias, void* out, int64_t ld_out, int64_t n_out,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * mxq_gemm_mixed -- the grouped GEMM for per-output-channel weight formats
+ * (Chameleon article, "hardware support" paragraph: mixed formats split the
+ * product into groups).  w_groups[g] holds the rows of format group g, in
+ * order; w_perm (device int32, sum of group rows) gives each grouped row's
+ * output column, group after group.  Each group runs mxq_gemm's route for
+ * its format on the same stream; the low-rank branch and bias, if given,
+ * are added exactly once per output column.
+ */
+mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int32_t n_groups,
+                          const int32_t* w_perm,
+                          const float* lr_u, int64_t ld_u, const void* lr_l2t, int32_t lr_rank,
+                          const void* bias, void* out, int64_t ld_out, int64_t n_out,
+                          void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * mxq_select_format -- per-output-channel weight format by least
+ * reconstruction error (Chameleon article, "the format is chosen by the
+ * value distribution").
+ *
+ *  w           device fp32 or bf16 weights [n][ldw], k columns used.
+ *  candidates  host array of n_cand formats (MXQ_FMT_INT4 / MXFP4 / NVFP4),
+ *              in tie-break order (earliest wins a tie).
+ *  choice_out  device uint8[n]: index into candidates of the chosen format.
+ *  sse_out     optional device float64 [n][n_cand]: sum over the row of
+ *              (w - dequant(quant(w)))^2, each squared difference exact.
+ *  perm_out    optional device int32[n]: rows grouped by chosen candidate in
+ *              candidate order, ascending row index inside a group.
+ *  counts_out  optional device int32[n_cand]: rows per candidate.
+ *  g_out       optional device float: the NVFP4 tensor scale over all of w
+ *              (the one the NVFP4 candidate used).
+ *  workspace   mxq_workspace_size(MXQ_OP_SELECT, n, k, 0) bytes.
+ * k must be a multiple of 32.
+ */
+mxq_status mxq_select_format(const void* w, int32_t dtype, int64_t n, int64_t k, int64_t ldw,
+                             const int32_t* candidates, int32_t n_cand,
+                             uint8_t* choice_out, double* sse_out, int32_t* perm_out,
+                             int32_t* counts_out, float* g_out,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * mxq_act_format_for_step -- host-only table read (Chameleon article: ten
+ * trajectory intervals; at inference routing is a table read).
+ * bucket = min(n_buckets - 1, floor(n_buckets * step / num_steps));
+ * returns table[layer * n_buckets + bucket], or -1 for invalid arguments
+ * (NULL table, layer outside [0, n_layers), step outside [0, num_steps)).
+ */
+int32_t mxq_act_format_for_step(const uint8_t* table, int32_t n_layers, int32_t n_buckets,
+                                int32_t layer, int32_t step, int32_t num_steps);
+
+/* Operations for mxq_workspace_size. */
+enum { MXQ_OP_QUANTIZE = 1, MXQ_OP_GEMM = 2, MXQ_OP_SELECT = 3 };
+
+/* Workspace bytes an operation needs for a [rows, cols] operand of format
+ * fmt (0 when none); returns -1 for unknown arguments.  Host-only. */
+int64_t mxq_workspace_size(int32_t op, int64_t rows, int64_t cols, int32_t fmt);
+
+/* Per-row storage of a format with cols elements per row: code bytes and
+ * scale bytes (the minimum ld_codes / ld_scales).  Returns MXQ_ERR_SHAPE if
+ * cols is not a multiple of the format's block.  Host-only. */
+mxq_status mxq_storage(int32_t fmt, int64_t cols, int64_t* code_bytes, int64_t* scale_bytes);
+
+/* Static description of a status code.  Host-only. */
+const char* mxq_status_string(int32_t status);
+
+/* MXQ_VERSION of the built library.  Host-only. */
+int32_t mxq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

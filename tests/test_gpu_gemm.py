@@ -1,0 +1,100 @@
+"""GPU parity: mxq_gemm on every supported (activation, weight) format pair,
+with and without bias, low-rank branch and column map, ragged M/N and long
+K, against the float64 oracle under the stated error bound.  Operands are the
+oracle's own codes, uploaded, so the GEMM is checked in isolation."""
+import numpy as np
+import pytest
+
+from fp8_quantized_linear_mxq_amd import workloads as wl
+from oracle import quantize as oq
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+ROUTES = [(a, w) for a in ("MXFP4", "MXFP8", "NVFP4") for w in ("MXFP4", "NVFP4", "INT4")]
+
+
+def _operands(m, n, k, fa, fw, seed):
+    rng = np.random.default_rng(seed)
+    a = rng.standard_t(3, size=(m, k)) * 2.0
+    a[:, rng.choice(k, size=max(1, k // 200), replace=False)] *= 50.0   # hot channels
+    a = a.astype(np.float32)
+    w = rng.normal(0, 0.02, size=(n, k)).astype(np.float32)
+    qa = oq.quantize(a, fa)
+    qw = oq.quantize(w, fw)
+    return qa, qw
+
+
+@pytest.mark.parametrize("variant", ["plain", "bias_lr", "colmap"])
+@pytest.mark.parametrize("fa,fw", ROUTES)
+def test_gemm_routes(fa, fw, variant):
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    m, n, k = 200, 300, 640
+    gu.say(f"gemm {fa}x{fw} {variant} M={m} N={n} K={k}")
+    qa, qw = _operands(m, n, k, fa, fw, seed=len(fa) * 7 + len(fw) + len(variant))
+    a_dev = gu.qtensor_from_oracle(qa, m, k)
+    w_dev = gu.qtensor_from_oracle(qw, n, k)
+    a_deq = gu.dequant_a_for_gemm(qa)
+    w_deq = gu.dequant_w_for_gemm(qw)
+    alpha = gu.alpha_of(qa, qw)
+    rng = np.random.default_rng(3)
+    if variant == "plain":
+        y = mxq.gemm(a_dev, w_dev)
+        gu.check_gemm(y, a_deq, w_deq, alpha, tag=f"{fa}x{fw}")
+    elif variant == "bias_lr":
+        r = 32
+        u = (rng.standard_normal((m, r)) * 4).astype(np.float32)
+        l2 = wl.bf16_to_f32(wl.f32_to_bf16_bits(rng.normal(0, 0.02, (r, n)).astype(np.float32)))
+        bias = wl.bf16_to_f32(wl.f32_to_bf16_bits(rng.normal(0, 1, n).astype(np.float32)))
+        y = mxq.gemm(a_dev, w_dev, u=gu.to_dev_f32(u),
+                     l2t=gu.to_dev_bf16(wl.f32_to_bf16_bits(np.ascontiguousarray(l2.T))),
+                     bias=gu.to_dev_bf16(wl.f32_to_bf16_bits(bias)))
+        # the low-rank term's bound: sum_j |u_j| |L2_jn| (u is given exactly here)
+        gu.check_gemm(y, np.hstack([a_deq, u.astype(np.float64)]),
+                      np.hstack([w_deq, l2.T.astype(np.float64) / alpha]), alpha,
+                      bias=bias, tag=f"{fa}x{fw} lr")
+    else:
+        n_out = n + 20
+        perm = rng.permutation(n_out)[:n].astype(np.int32)
+        out = torch.full((m, n_out), -7.0, dtype=torch.bfloat16, device="cuda")
+        y = mxq.gemm(a_dev, w_dev, n_out=n_out,
+                     w_out_col=torch.from_numpy(perm).cuda(), out=out)
+        yh = y.float().cpu().numpy()
+        untouched = np.setdiff1d(np.arange(n_out), perm)
+        assert np.all(yh[:, untouched] == -7.0)
+        gu.check_gemm(y, a_deq, w_deq, alpha, cols=perm, tag=f"{fa}x{fw} colmap")
+
+
+@pytest.mark.parametrize("fa,fw", ROUTES)
+def test_gemm_long_k(fa, fw):
+    """K = 8192 exercises the fp32 slab accumulation of every route."""
+    import fp8_quantized_linear_mxq_amd as mxq
+    m, n, k = 64, 96, 8192
+    gu.say(f"gemm long K {fa}x{fw} M={m} N={n} K={k}")
+    qa, qw = _operands(m, n, k, fa, fw, seed=11)
+    y = mxq.gemm(gu.qtensor_from_oracle(qa, m, k), gu.qtensor_from_oracle(qw, n, k))
+    r = gu.check_gemm(y, gu.dequant_a_for_gemm(qa), gu.dequant_w_for_gemm(qw),
+                      gu.alpha_of(qa, qw), tag=f"{fa}x{fw} longK")
+    gu.say(f"  worst err/tol {r:.3g}")
+
+
+def test_gemm_errors():
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    gu.say("gemm argument errors")
+    qa, qw = _operands(8, 8, 128, "INT4", "MXFP4", seed=1)
+    with pytest.raises(mxq.MxqError) as ei:
+        mxq.gemm(gu.qtensor_from_oracle(qa, 8, 128), gu.qtensor_from_oracle(qw, 8, 128))
+    assert ei.value.status == 2                      # INT4 activations: unsupported
+    a160 = mxq.empty_qtensor(mxq.MXFP4, 8, 160)      # padded, aligned row strides
+    w160 = mxq.empty_qtensor(mxq.MXFP4, 8, 160)
+    with pytest.raises(mxq.MxqError) as ei:
+        mxq.gemm(a160, w160)
+    assert ei.value.status == 4                      # K not a multiple of 128
+    # M = 0 is a no-op
+    qa, qw = _operands(1, 8, 128, "MXFP4", "MXFP4", seed=1)
+    a0 = gu.qtensor_from_oracle(qa, 1, 128)
+    a0.rows = 0
+    out = torch.zeros((0, 8), dtype=torch.bfloat16, device="cuda")
+    mxq.gemm(a0, gu.qtensor_from_oracle(qw, 8, 128), out=out)

@@ -1,0 +1,115 @@
+"""GPU parity: mxq_quantize (all formats, both input dtypes, every Hadamard
+size) against the oracle, bit-exact on codes, scales and tensor scale."""
+import numpy as np
+import pytest
+
+from fp8_quantized_linear_mxq_amd import workloads as wl
+from oracle import quantize as oq
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = ["MXFP4", "MXFP8", "NVFP4", "INT4"]
+
+
+def _inputs(rows, cols, dtype, seed, had):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_t(3, size=(rows, cols))
+    x *= 2.0 ** rng.integers(-12, 12, size=(rows, 1))
+    hot = rng.random((rows, cols)) < 0.003
+    x = np.where(hot, x * 100.0, x)
+    if had:
+        # keep each rotation block's dynamic range inside the exact-sum contract
+        scale = 2.0 ** np.floor(np.log2(np.abs(x).max(axis=1, keepdims=True)))
+        x = np.sign(x) * np.maximum(np.abs(x), scale * 2.0 ** -12)
+    x[0, :] = 0.0
+    x[0, 1::3] = -0.0
+    x[1, :] = (1.0 + rng.random(cols)) * 2.0 ** -128 * rng.choice([-1, 1], cols)  # subnormals
+    if had == 0:
+        # exact grid midpoints and saturation cases in MX blocks (scale 2**0)
+        x[2, :32] = [6.0, 5.0, 3.5, 2.5, 1.75, 1.25, 0.75, 0.25] * 4
+        x[2, 32:64] = [448.0, 464.0, 460.0, 1.0625, 1.1875, 17.0, 0.0009765625, 300.0] * 4
+        x[3, :] = rng.standard_normal(cols) * 1e30
+    x = x.astype(np.float32)
+    if dtype == "bf16":
+        bits = wl.f32_to_bf16_bits(x)
+        return bits, wl.bf16_to_f32(bits)
+    return x, x
+
+
+@pytest.mark.parametrize("had", [0, 16, 32, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_quantize_matches_oracle(fmt, dtype, had):
+    import fp8_quantized_linear_mxq_amd as mxq
+    rows, cols = 37, 384
+    raw, vals = _inputs(rows, cols, dtype, seed=hash((fmt, dtype, had)) % 1000, had=had)
+    gu.say(f"quantize fmt={fmt} dtype={dtype} had={had} shape={rows}x{cols}")
+    xd = gu.act_to_dev(raw, dtype)
+    q = mxq.quantize(xd, gu.FMT_ID[fmt], hadamard=had)
+    want = gu.oracle_quant(vals, fmt, had, mant_bits=7 if dtype == "bf16" else 23)
+    got_codes = gu.unpack_dev_codes(q, fmt)
+    got_scales = gu.dev_scales(q, fmt)
+    if fmt == "NVFP4":
+        assert float(q.tensor_scale.cpu()[0]) == float(want["g"])
+    bad = np.argwhere(got_scales != want["scales"])
+    assert bad.size == 0, f"scale mismatch at {bad[:5].tolist()}"
+    bad = np.argwhere(got_codes != want["codes"])
+    assert bad.size == 0, (f"code mismatch at {bad[:5].tolist()}: got "
+                           f"{got_codes[tuple(bad[0])]} want {want['codes'][tuple(bad[0])]}")
+
+
+def test_nvfp4_static_scale_and_strided_rows():
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    rng = np.random.default_rng(5)
+    x = (rng.laplace(size=(50, 256 + 64)) * 3).astype(np.float32)
+    xd = gu.to_dev_f32(x)[:, :256]                    # row stride 320 elements
+    g = np.float32(0.0017)
+    gd = torch.tensor([g], dtype=torch.float32).cuda()
+    gu.say("quantize NVFP4 static g, strided rows")
+    q = mxq.quantize(xd, mxq.NVFP4, static_tensor_scale=gd)
+    want = oq.quantize(x[:, :256], "NVFP4", tensor_scale=g)
+    assert np.array_equal(gu.dev_scales(q, "NVFP4"), want["scales"])
+    assert np.array_equal(gu.unpack_dev_codes(q, "NVFP4"), want["codes"])
+    assert float(q.tensor_scale.cpu()[0]) == float(g)
+
+
+def test_edge_shapes():
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    gu.say("quantize edge shapes")
+    # one block, one row
+    x = np.array([[7.5] + [0.0] * 30 + [-0.3]], np.float32)
+    q = mxq.quantize(gu.to_dev_f32(x), mxq.MXFP4)
+    want = oq.quantize(x, "MXFP4")
+    assert np.array_equal(gu.unpack_dev_codes(q, "MXFP4"), want["codes"])
+    # empty input is a no-op
+    e = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    q = mxq.quantize(e, mxq.MXFP8)
+    assert q.rows == 0
+    # shape errors are reported, nothing is launched
+    with pytest.raises(mxq.MxqError) as ei:
+        mxq.quantize(gu.to_dev_f32(np.zeros((2, 48), np.float32)), mxq.MXFP4)
+    assert ei.value.status == 4
+    with pytest.raises(mxq.MxqError):
+        mxq.quantize(gu.to_dev_f32(np.zeros((2, 96), np.float32)), mxq.MXFP4, hadamard=64)
+
+
+def test_lowrank_down():
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    rng = np.random.default_rng(8)
+    m, k, r = 100, 640, 32
+    xb = wl.f32_to_bf16_bits((rng.standard_t(3, size=(m, k))).astype(np.float32))
+    l1 = wl.f32_to_bf16_bits(rng.normal(0, 0.02, size=(k, r)).astype(np.float32))
+    l1t = np.ascontiguousarray(l1.T)
+    u = torch.empty((m, r), dtype=torch.float32, device="cuda")
+    gu.say("quantize + fused low-rank down projection")
+    mxq.quantize(gu.to_dev_bf16(xb), mxq.MXFP4, l1t=gu.to_dev_bf16(l1t), u=u)
+    xv = wl.bf16_to_f32(xb).astype(np.float64)
+    lv = wl.bf16_to_f32(l1).astype(np.float64)
+    ref = xv @ lv
+    bound = np.abs(xv) @ np.abs(lv)
+    err = np.abs(u.cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= 1e-5 * bound), float(np.max(err / bound))
