@@ -1,0 +1,274 @@
+"""Benchmark: one quantized linear layer step on one MI355X.
+
+A step is one pass of the layer's hot path over a batch of synthetic input:
+[rotate +] quantize the activations (and the fused low-rank down projection
+where the layer has one), then the block-scaled GEMM against weights that
+were quantized beforehand (weights are prepared once per layer, outside the
+timed region).  Inputs are resident in HBM before timing starts; the timed
+steps cycle through enough independent buffer sets (activations, codes,
+weights, outputs) that the working set exceeds 512 MB, twice the 256 MB
+Infinity Cache, so every step reads from HBM.
+
+Prints one JSON line.  ``value`` is whole-step GEMM throughput (2 M N K per
+step / step time) in TFLOP/s.  ``roofline`` describes the dominant kernel
+(the GEMM), timed per launch with HIP events on its stream; ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from fp8_quantized_linear_mxq_amd import workloads as wl  # noqa: E402
+
+PEAK_TFLOPS = {"mxfp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0, "fp16": 2500.0}
+HBM_GBPS = 8000.0
+DEFAULT_WORKLOAD = "w4a8_mlp"
+CSRC = os.path.join(ROOT, "fp8_quantized_linear_mxq_amd", "csrc")
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def gemm_dtype(act_fmt: str, w_fmt: str) -> str:
+    if act_fmt == "MXFP4" and w_fmt == "MXFP4":
+        return "mxfp4"
+    if act_fmt == "NVFP4" and w_fmt == "NVFP4":
+        return "fp16"
+    return "bf16"
+
+
+def quantize_bytes(w: wl.Workload) -> int:
+    """Algorithmic HBM bytes of one activation quantize: read x, write codes
+    and scales (and u for the low-rank branch)."""
+    esz = 2 if w.act_dtype == "bf16" else 4
+    rd = w.m * w.k * esz
+    code = w.m * w.k // (1 if w.act_fmt == "MXFP8" else 2)
+    scale = w.m * w.k // (16 if w.act_fmt == "NVFP4" else 32)
+    wr = code + scale + (w.m * w.rank * 4 if w.rank else 0)
+    if w.act_fmt == "NVFP4":
+        rd *= 2            # the dynamic tensor scale needs a first pass over x
+    return rd + wr
+
+
+def make_sets(w: wl.Workload, n_sets: int, mxq, torch):
+    """Device buffer sets: activations, pre-quantized weights, outputs."""
+    act = wl.activations(w)
+    wt = wl.weights(w)
+    fa, fw = wl_fmt(mxq, w.act_fmt), wl_fmt(mxq, w.w_fmt)
+    if w.act_dtype == "bf16":
+        x0 = torch.from_numpy(act.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        x0 = torch.from_numpy(act).cuda()
+    w0 = torch.from_numpy(wt).cuda()
+    l1t = l2t = None
+    if w.rank:
+        l1, l2 = wl.lowrank_factors(w)
+        l1t = torch.from_numpy(np.ascontiguousarray(l1.T).view(np.int16)).view(torch.bfloat16).cuda()
+        l2t = torch.from_numpy(np.ascontiguousarray(l2.T).view(np.int16)).view(torch.bfloat16).cuda()
+    sets = []
+    for i in range(n_sets):
+        x = x0.clone()
+        qw = mxq.quantize(w0, fw, hadamard=w.hadamard)
+        qa = mxq.empty_qtensor(fa, w.m, w.k)
+        ws = torch.empty((max(16, mxq.workspace_size(1, w.m, w.k, fa)),), dtype=torch.uint8, device="cuda")
+        out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
+        u = torch.empty((w.m, w.rank), dtype=torch.float32, device="cuda") if w.rank else None
+        sets.append(dict(x=x, qw=qw, qa=qa, ws=ws, out=out, u=u,
+                         l1t=l1t.clone() if l1t is not None else None,
+                         l2t=l2t.clone() if l2t is not None else None))
+    del w0
+    torch.cuda.synchronize()
+    return sets
+
+
+def wl_fmt(mxq, name: str) -> int:
+    return {"MXFP4": mxq.MXFP4, "MXFP8": mxq.MXFP8, "NVFP4": mxq.NVFP4, "INT4": mxq.INT4}[name]
+
+
+def set_bytes(s) -> int:
+    tot = 0
+    for v in s.values():
+        if v is None:
+            continue
+        if hasattr(v, "codes"):
+            for t in (v.codes, v.scales, v.tensor_scale):
+                if t is not None:
+                    tot += t.numel() * t.element_size()
+        else:
+            tot += v.numel() * v.element_size()
+    return tot
+
+
+def cpu_baseline(w: wl.Workload, budget_s: float = 15.0) -> dict:
+    """The oracle, as it stands, on a bounded row sample of the workload:
+    activation quantize + float64 GEMM (+ low-rank branch) per row."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import gemm as og
+    from oracle import hadamard as oh
+    from oracle import quantize as oq
+    from oracle.formats import round_to_bf16
+
+    wt = wl.weights(w)
+    w_rot = oh.rotate(wt, w.hadamard, 7) if w.hadamard else wt
+    qw = oq.quantize(w_rot, w.w_fmt)
+    w_deq = oq.dequantize(qw)
+    if w.rank:
+        l1, l2 = wl.lowrank_factors(w)
+        l1v = wl.bf16_to_f32(l1).astype(np.float64)
+        l2v = wl.bf16_to_f32(l2).astype(np.float64)
+    rows = 64
+    done_rows, elapsed = 0, 0.0
+    act = wl.activations(w, rows=min(w.m, 4096))
+    vals = wl.bf16_to_f32(act) if w.act_dtype == "bf16" else act
+    while elapsed < budget_s and done_rows < vals.shape[0]:
+        chunk = vals[done_rows:done_rows + rows]
+        t0 = time.perf_counter()
+        r = oh.rotate(chunk, w.hadamard, 7) if w.hadamard else chunk
+        qa = oq.quantize(r, w.act_fmt)
+        y = og.linear(oq.dequantize(qa), w_deq)
+        if w.rank:
+            y = y + og.lowrank_down(chunk, l1v) @ l2v
+        round_to_bf16(y)
+        elapsed += time.perf_counter() - t0
+        done_rows += chunk.shape[0]
+        rows = min(rows * 2, 1024)
+    flops = 2.0 * done_rows * w.n * w.k
+    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done_rows} of {w.m} rows: oracle {w.act_fmt} quantize"
+                      f"{' + H' + str(w.hadamard) if w.hadamard else ''} + float64 GEMM "
+                      f"against {w.w_fmt} weights{' + rank-' + str(w.rank) + ' branch' if w.rank else ''}"
+                      f", {elapsed:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the layer shards by output channels; see the design notes)", file=sys.stderr)
+        return 2
+    w = wl.WORKLOADS[args.workload]
+    if w.w_fmt == "MIXED":
+        print("the mixed-format convolution layer is a parity-test case, not a bench line",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import fp8_quantized_linear_mxq_amd as mxq
+    mxq.load()
+    torch.cuda.set_device(0)
+    one = make_sets(w, 1, mxq, torch)
+    per_set = set_bytes(one[0])
+    n_sets = max(2, int(np.ceil(512e6 / per_set)) + 1)
+    sets = one + make_sets(w, n_sets - 1, mxq, torch)
+    fa = wl_fmt(mxq, w.act_fmt)
+    stream = torch.cuda.current_stream()
+
+    def step(s, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        mxq.quantize(s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], u=s["u"], out=s["qa"],
+                     workspace=s["ws"])
+        if ev is not None:
+            ev[1].record(stream)
+        mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"])
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(args.warmup):
+        step(sets[i % n_sets])
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, wall clock, synchronized both sides
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % n_sets])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-kernel durations with events on the launch stream (separate pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(sets[i % n_sets], evs[i])
+    torch.cuda.synchronize()
+    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    if args.copy_probe:
+        a = torch.empty((1 << 28,), dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    ms = wall / args.steps * 1e3
+    flops = 2.0 * w.m * w.n * w.k + (2.0 * w.m * w.n * 2 * w.rank if w.rank else 0.0)
+    gdt = gemm_dtype(w.act_fmt, w.w_fmt)
+    achieved = flops / (g_ms * 1e-3) / 1e12
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        ent = t.get(w.name)
+        if ent and ent.get("kernel_source_digest") == kernel_source_digest():
+            traffic = ent.get("gemm_hbm_bytes_per_launch")
+    qbytes = quantize_bytes(w)
+    rec = {
+        "metric": "block-scaled GEMM TFLOP/s & % MXFP4 peak; quantize GB/s & % HBM BW",
+        "value": round(2.0 * w.m * w.n * w.k / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": gdt,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.m, "K": w.k, "N": w.n,
+                   "activations": f"{w.act_dtype} -> {w.act_fmt}", "weights": w.w_fmt,
+                   "hadamard": w.hadamard, "lowrank": w.rank, "buffer_sets": n_sets,
+                   "working_set_MB": round(n_sets * per_set / 1e6, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_TFLOPS[gdt], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS[gdt], 4), "traffic": traffic,
+                     "kernel": "gemm", "avg_launch_us": round(g_ms * 1e3, 3)},
+        "gemm_pct_mxfp4_peak": round(achieved / PEAK_TFLOPS["mxfp4"], 4),
+        "quantize": {"avg_launch_us": round(q_ms * 1e3, 3), "algorithmic_bytes": qbytes,
+                     "GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(qbytes / (q_ms * 1e-3) / 1e9 / HBM_GBPS, 4)},
+        "kernel_source_digest": kernel_source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
