@@ -1,4 +1,5 @@
-// Block-scaled GEMM on the gfx950 scaled MFMA: y = RN_bf16(Q(a) Q(w)^T [+ u L2] [+ bias]).
+// Block-scaled GEMM on the gfx950 scaled MFMA for MXFP4 activations x MXFP4
+// weights: y = RN_bf16(Q(a) Q(w)^T [+ u L2] [+ bias]).
 //
 // The 4-bit weight x 4-bit activation product is the layer's one dense
 // contraction (Nunchaku article, "main explanation": W4A4 speeds up the
@@ -7,187 +8,230 @@
 // one E8M0 scale per lane per 32 K-values, which is exactly the MX block
 // (Microscaling FP4 summary: power-of-two MXFP4 scales), so codes and scales
 // go from HBM to the matrix core with no conversion.  For E2M1 x E2M1 its
-// dot products are exact before the fp32 accumulation (measured); with E4M3
-// operands they are not, so MXFP8 activations take the dequantizing route.
-// The kernel keeps the E4M3 operand path (AF = 0) for completeness.
+// dot products are exact before the fp32 accumulation (measured).
 //
-// Operand layouts (checked on gfx950): lane l of a 32x32x64 step holds row
-// l % 32; for E2M1 its 32 codes are K = 32*(l/32) + [0,32); for E4M3 they are
-// split 16 + 16 (see the A-fragment load).  Either way the lane's scale
-// register supplies the E8M0 of K-block l/32 of its row.
+// Operand layout (checked on gfx950): lane l of a 32x32x64 step holds row
+// l % 32 and the 32 E2M1 codes K = 32*(l/32) + [0,32), i.e. 16 bytes; its
+// scale register supplies the E8M0 of that row's K-block l/32, the byte
+// chosen by op_sel.
 //
-// Tiling: 128x128 output tile per 256-thread workgroup, 2x2 waves of 64x64,
-// each wave 2x2 MFMA tiles of 32x32; K-tile 128 (two MFMA K-steps of 64).
-// Codes are staged through double-buffered LDS with a 16-byte-chunk XOR
-// swizzle; the per-row scale bytes of a K-tile (4 blocks) are one dword
-// loaded straight into registers, and the MFMA op_sel picks the byte.
-// Workgroup ids are remapped so each XCD works on a contiguous tile range.
+// Organisation:
+//  * workgroup tile (64*TM) x (64*TN), four waves in a 2 x 2 grid, each wave
+//    (32*TM) x (32*TN) = TM*TN MFMA tiles; K-tile 128 (two MFMA K-steps);
+//  * code and scale tiles stream into a 3-stage LDS ring with direct
+//    global->LDS loads three K-tiles ahead of the MFMAs (no register
+//    staging); each lane's load address is chosen so the bytes land in the
+//    XOR-swizzled slot the fragment reads expect;
+//  * fragments of K-tile kt+1 are read from LDS while the MFMAs of K-tile kt
+//    run; one barrier per K-tile;
+//  * the MFMAs compute D^T = W A^T (weight fragment first), so each lane ends
+//    up holding four consecutive output columns of one row;
+//  * past 32 K-tiles (K > 4096) the fp32 chains are flushed into a second
+//    accumulator every 16 K-tiles (small tiles only, for the registers).
 #include "device_common.h"
-#include "kernels.h"
 #include "gemm_common.h"
+#include "gemm_pipe.h"
+#include "kernels.h"
 
 namespace mxq {
 namespace {
 
-constexpr int BK = 128;
-constexpr int kSlabTiles = 16;   // K-tiles (2 MFMA steps each) per fp32 slab
+constexpr int BK = 128;           // K per tile
+constexpr int RB = BK / 2;        // bytes per row per K-tile (E2M1)
+constexpr int CH = RB / 16;       // 16-byte chunks per row
+constexpr int kSlab = 16;         // K-tiles per fp32 slab when slabbing
 
-// AF: MFMA format code of the activation codes (0 = E4M3, 4 = E2M1).
-template <int AF, bool LR, bool SLAB>
-__global__ __launch_bounds__(kThreads) void gemm_mx_kernel(GemmP p) {
-  constexpr int A_RB = (AF == 4) ? 64 : 128;  // bytes per row per K-tile
-  constexpr int B_RB = 64;
-  constexpr int A_CH = A_RB / 16, B_CH = B_RB / 16;
-  constexpr int A_LOADS = BM * A_CH / kThreads, B_LOADS = BN * B_CH / kThreads;
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * A_RB];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * B_RB];
+}  // namespace
 
-  const int tile = remap_tile(blockIdx.x, p.tiles_m * p.tiles_n);
-  const int m0 = (tile / p.tiles_n) * BM, n0 = (tile % p.tiles_n) * BN;
+__device__ uint8_t g_zero16[16];
+
+namespace {
+
+template <int TM, int TN, bool SLAB, bool LR>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
+  constexpr int TBM = 64 * TM, TBN = 64 * TN;
+  constexpr int A_STAGE = TBM * RB, W_STAGE = TBN * RB;
+  constexpr int S_STAGE = scale_region_bytes<TBM, 4, TBN, 4>();
+  constexpr int STAGE = A_STAGE + W_STAGE + S_STAGE;
+  constexpr int NT = (TBM + TBN) * CH / 256 + S_STAGE / 1024;   // loads per wave per K-tile
+  // three separate arrays: reads of one stage are visibly independent of the
+  // loads in flight into the others, so the compiler adds no wait for them
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, gm, tm, tn);
+  const int m0 = tm * TBM, n0 = tn * TBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, half = lane >> 5;
   const int KT = p.K / BK;
 
-  // global -> LDS chunk assignment
-  const uint8_t* ga[A_LOADS];
-  int la[A_LOADS];
-  bool va[A_LOADS];
+  // byte offsets within a stage of this lane's fragment and scale reads
+  uint32_t a_off[TM][2], w_off[TN][2], sa_off[TM], sw_off[TN];
 #pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int q = tid + i * kThreads, r = q / A_CH, c = q % A_CH;
-    va[i] = (m0 + r) < p.M;
-    ga[i] = p.a + (int64_t)(va[i] ? m0 + r : 0) * p.lda + c * 16;
-    la[i] = r * A_RB + ((c ^ swz<A_CH>(r)) * 16);
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * 32 * TM + i * 32 + l32;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) a_off[i][s] = r * RB + (((2 * s + half) ^ swz<CH>(r)) * 16);
+    sa_off[i] = A_STAGE + W_STAGE + r * 4;
   }
-  const uint8_t* gb[B_LOADS];
-  int lb[B_LOADS];
-  bool vb[B_LOADS];
 #pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int q = tid + i * kThreads, r = q / B_CH, c = q % B_CH;
-    vb[i] = (n0 + r) < p.N;
-    gb[i] = p.w + (int64_t)(vb[i] ? n0 + r : 0) * p.ldw + c * 16;
-    lb[i] = r * B_RB + ((c ^ swz<B_CH>(r)) * 16);
-  }
-  // scale rows for this lane's MFMA fragments (clamped; results discarded)
-  const uint8_t* sa_row[2];
-  const uint8_t* sb_row[2];
+  for (int j = 0; j < TN; ++j) {
+    const int r = wn * 32 * TN + j * 32 + l32;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int r = m0 + wm * 64 + i * 32 + l32;
-    sa_row[i] = p.as + (int64_t)(r < p.M ? r : p.M - 1) * p.ldas;
-    int c = n0 + wn * 64 + i * 32 + l32;
-    sb_row[i] = p.ws + (int64_t)(c < p.N ? c : p.N - 1) * p.ldws;
+    for (int s = 0; s < 2; ++s) w_off[j][s] = A_STAGE + r * RB + (((2 * s + half) ^ swz<CH>(r)) * 16);
+    sw_off[j] = A_STAGE + W_STAGE + (TBM + r) * 4;
   }
 
-  uint4 ra[A_LOADS], rb[B_LOADS];
-  uint32_t sa[2], sb[2], nsa[2], nsb[2];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      ra[i] = va[i] ? *reinterpret_cast<const uint4*>(ga[i] + (int64_t)kt * A_RB)
-                    : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      rb[i] = vb[i] ? *reinterpret_cast<const uint4*>(gb[i] + (int64_t)kt * B_RB)
-                    : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      nsa[i] = *reinterpret_cast<const uint32_t*>(sa_row[i] + kt * 4) >> (8 * half);
-      nsb[i] = *reinterpret_cast<const uint32_t*>(sb_row[i] + kt * 4) >> (8 * half);
-    }
+  auto issue = [&](int kt, uint8_t* st) {
+    const bool past = kt >= KT;   // past the end of K: a tile of zeros
+    kt = past ? KT - 1 : kt;
+    issue_tile<TBM, RB>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past);
+    issue_tile<TBN, RB>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past);
+    issue_scale_tile<TBM, 4, TBN, 4>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane, past);
   };
-  auto lstore = [&](int buf) {
+  struct Frag {
+    v4i a[TM][2], w[TN][2];
+    uint32_t sa[TM], sw[TN];
+  };
+  auto read = [&](const uint8_t* st, Frag& f) {
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<uint4*>(&sA[buf][la[i]]) = ra[i];
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) *reinterpret_cast<uint4*>(&sB[buf][lb[i]]) = rb[i];
+      for (int s = 0; s < 2; ++s) f.a[i][s] = *reinterpret_cast<const v4i*>(st + a_off[i][s]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) f.w[j][s] = *reinterpret_cast<const v4i*>(st + w_off[j][s]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) f.sa[i] = *reinterpret_cast<const uint32_t*>(st + sa_off[i]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) f.sw[j] = *reinterpret_cast<const uint32_t*>(st + sw_off[j]);
   };
 
-  v16f acc[2][2], tot[2][2];
+  v16f acc[TM][TN];
+  v16f tot[SLAB ? TM : 1][SLAB ? TN : 1];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[i][j] = v16f{};
-      tot[i][j] = v16f{};
-    }
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+  if constexpr (SLAB) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) tot[i][j] = v16f{};
+  }
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
+  auto compute = [&](const Frag& f) {
+    // the lane's E8M0 bytes for K-blocks 2s + half sit at byte 2s after the shift
+    uint32_t sa[TM], sw[TN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) { sa[i] = nsa[i]; sb[i] = nsb[i]; }
-    if (kt + 1 < KT) gload(kt + 1);
+    for (int i = 0; i < TM; ++i) sa[i] = f.sa[i] >> (8 * half);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v8i af[2], bf[2];
+    for (int j = 0; j < TN; ++j) sw[j] = f.sw[j] >> (8 * half);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + l32;
-        if constexpr (AF == 4) {
-          const int c = s * 2 + half;
-          const uint4 v = *reinterpret_cast<const uint4*>(&sA[buf][r * A_RB + ((c ^ swz<A_CH>(r)) * 16)]);
-          af[i] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
-        } else {
-          // E4M3 operand layout: dwords 0-3 hold K = 16*half + [0,16), dwords
-          // 4-7 hold K = 32 + 16*half + [0,16) of this 64-wide K step
-          const int c0 = s * 4 + half, c1 = s * 4 + 2 + half;
-          const uint4 v0 = *reinterpret_cast<const uint4*>(&sA[buf][r * A_RB + ((c0 ^ swz<A_CH>(r)) * 16)]);
-          const uint4 v1 = *reinterpret_cast<const uint4*>(&sA[buf][r * A_RB + ((c1 ^ swz<A_CH>(r)) * 16)]);
-          af[i] = v8i{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                      (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-        }
-        const int rb2 = wn * 64 + i * 32 + l32;
-        const int cb = s * 2 + half;
-        const uint4 w = *reinterpret_cast<const uint4*>(&sB[buf][rb2 * B_RB + ((cb ^ swz<B_CH>(rb2)) * 16)]);
-        bf[i] = v8i{(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
-      }
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < TN; ++j) {
+          // E2M1 operands use the low four dwords of the 8-dword register
+          const v8i wv = __builtin_shufflevector(f.w[j][s], f.w[j][s], 0, 1, 2, 3, -1, -1, -1, -1);
+          const v8i av = __builtin_shufflevector(f.a[i][s], f.a[i][s], 0, 1, 2, 3, -1, -1, -1, -1);
           if (s == 0)
-            acc[i][j] = mfma_scaled<0, AF>(af[i], bf[j], acc[i][j], (int)sa[i], (int)sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                wv, av, acc[i][j], 4, 4, 0, (int)sw[j], 0, (int)sa[i]);
           else
-            acc[i][j] = mfma_scaled<2, AF>(af[i], bf[j], acc[i][j], (int)sa[i], (int)sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                wv, av, acc[i][j], 4, 4, 2, (int)sw[j], 2, (int)sa[i]);
         }
+  };
+
+  // One K-tile.  On entry `cur` holds (or is receiving) K-tile kt's
+  // fragments and K-tiles kt+1, kt+2 are in flight into their stages (tile t
+  // lives in stage t % 3).
+  //  - wait until K-tile kt+1 has landed (kt+2 may still be in flight) and
+  //    this wave's reads of kt are complete, then barrier: every wave is done
+  //    reading stage kt % 3;
+  //  - read K-tile kt+1 into `nxt`, load K-tile kt+3 into the stage just
+  //    freed, and multiply K-tile kt, the reads and loads issued in the
+  //    shadow of the MFMAs.
+  // The loop runs a whole number of 6-step groups with no branch (which keeps
+  // the accumulators in place and each step one scheduling region); K-tiles
+  // past the end are loaded as zeros and add nothing.
+  constexpr int N_MFMA = 2 * TM * TN;
+  constexpr int N_DS = 2 * (TM + TN) + TM + TN;
+  auto step = [&](int kt, const uint8_t* st_next, uint8_t* st_cur, const Frag& cur, Frag& nxt) {
+    wait_vmcnt<NT>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    read(st_next, nxt);
+    issue(kt + 3, st_cur);
+    compute(cur);
+    // interleave: two LDS reads and one global->LDS load per MFMA up front
+#pragma unroll
+    for (int k = 0; k < N_MFMA; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (2 * k < N_DS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (k < NT) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     if constexpr (SLAB) {
-      if ((kt + 1) % kSlabTiles == 0) {
+      if (kt < KT && (kt + 1) % kSlab == 0) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
+          for (int j = 0; j < TN; ++j) {
             tot[i][j] += acc[i][j];
             acc[i][j] = v16f{};
           }
       }
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  wait_vmcnt<2 * NT>();
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  read(st0, f0);
+  for (int kt = 0; kt < KT; kt += 6) {
+    step(kt, st1, st0, f0, f1);
+    step(kt + 1, st2, st1, f1, f0);
+    step(kt + 2, st0, st2, f0, f1);
+    step(kt + 3, st1, st0, f1, f0);
+    step(kt + 4, st2, st1, f0, f1);
+    step(kt + 5, st0, st2, f1, f0);
   }
+  wait_vmcnt<0>();   // the spare loads issued past the end
   if constexpr (SLAB) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] += tot[i][j];
+      for (int j = 0; j < TN; ++j) acc[i][j] += tot[i][j];
   }
-  epilogue<LR>(p, acc, 1.0f, m0, n0, wm, wn, lane);
+  // the stages are free once every wave is past its last fragment read;
+  // each wave stages its output rows in its own slice of one of them
+  wait_lgkmcnt0();
+  __syncthreads();
+  static_assert(2 * 32 * (TN * 64 + 16) <= STAGE, "two staging slices per stage");
+  uint8_t* region = (wave < 2 ? st0 : st1) + (wave & 1) * 32 * (TN * 64 + 16);
+  epilogue_tr<LR, TM, TN>(p, acc, 1.0f, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
 }
 
-template <int AF>
-hipError_t dispatch(bool lr, bool slab, dim3 grid, const GemmP& p, hipStream_t s) {
-  if (lr) {
-    if (slab) gemm_mx_kernel<AF, true, true><<<grid, kThreads, 0, s>>>(p);
-    else gemm_mx_kernel<AF, true, false><<<grid, kThreads, 0, s>>>(p);
-  } else {
-    if (slab) gemm_mx_kernel<AF, false, true><<<grid, kThreads, 0, s>>>(p);
-    else gemm_mx_kernel<AF, false, false><<<grid, kThreads, 0, s>>>(p);
-  }
+template <int TM, int TN, bool SLAB>
+hipError_t launch_cfg(bool lr, GemmP p, hipStream_t s) {
+  p.tiles_m = (p.M + 64 * TM - 1) / (64 * TM);
+  p.tiles_n = (p.N + 64 * TN - 1) / (64 * TN);
+  const int tiles = p.tiles_m * p.tiles_n;
+  // tile-rows per group: one XCD's share (tiles / 8) as a near-square block
+  int gm = 1;
+  while (gm * 2 <= p.tiles_m && gm * 2 * gm * 2 <= (tiles + 7) / 8) gm *= 2;
+  const dim3 grid(tiles);
+  if (lr) gemm_mx_kernel<TM, TN, SLAB, true><<<grid, kThreads, 0, s>>>(p, gm);
+  else gemm_mx_kernel<TM, TN, SLAB, false><<<grid, kThreads, 0, s>>>(p, gm);
   return hipGetLastError();
 }
 
@@ -198,16 +242,25 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
   p.a = a.a_codes; p.lda = a.lda; p.as = a.a_scales; p.ldas = a.ld_as;
   p.w = a.w_codes; p.ldw = a.ldw; p.ws = a.w_scales; p.ldws = a.ld_ws;
   p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K;
-  p.tiles_m = (int)((a.M + BM - 1) / BM);
-  p.tiles_n = (int)((a.N + BN - 1) / BN);
   p.col_map = a.col_map;
   p.u = a.u; p.ld_u = a.ld_u; p.l2t = a.l2t; p.rank = a.rank;
   p.bias = a.bias;
   p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
-  const dim3 grid(p.tiles_m * p.tiles_n);
   const bool lr = a.rank > 0;
-  const bool slab = (a.K / BK) > 2 * kSlabTiles;
-  return dispatch<4>(lr, slab, grid, p, s);
+  if (a.K / BK > 2 * kSlab) return launch_cfg<2, 2, true>(lr, p, s);
+  // Large tiles move the fewest bytes per MFMA; pick the one whose tile count
+  // fills the 256 compute units in the fewest rounds, per unit of tile work.
+  const int64_t cu = 256;
+  auto rounds = [&](int tbm, int tbn) {
+    const int64_t t = ((a.M + tbm - 1) / tbm) * ((a.N + tbn - 1) / tbn);
+    return (t + cu - 1) / cu;
+  };
+  const int64_t c43 = rounds(256, 192) * 12 * 10;   // 4x3 MFMA tiles per wave
+  const int64_t c44 = rounds(256, 256) * 16 * 10;
+  const int64_t c22 = rounds(128, 128) * 4 * 16;    // small tiles run ~60% as efficiently
+  if (c22 < c43 && c22 < c44) return launch_cfg<2, 2, false>(lr, p, s);
+  if (c44 < c43) return launch_cfg<4, 4, false>(lr, p, s);
+  return launch_cfg<4, 3, false>(lr, p, s);
 }
 
 }  // namespace mxq

@@ -98,3 +98,26 @@ def test_gemm_errors():
     a0.rows = 0
     out = torch.zeros((0, 8), dtype=torch.bfloat16, device="cuda")
     mxq.gemm(a0, gu.qtensor_from_oracle(qw, 8, 128), out=out)
+
+
+# Shapes that make the MXFP4 x MXFP4 route pick each of its workgroup tiles
+# (128x128, 256x192, 256x256), all with ragged M and N tails.
+MX_TILE_SHAPES = [(130, 250, 384), (2000, 2300, 256), (4000, 4000, 256)]
+
+
+@pytest.mark.parametrize("m,n,k", MX_TILE_SHAPES)
+def test_gemm_mx_tiles(m, n, k):
+    import fp8_quantized_linear_mxq_amd as mxq
+    gu.say(f"gemm MXFP4xMXFP4 tiles M={m} N={n} K={k}")
+    qa, qw = _operands(m, n, k, "MXFP4", "MXFP4", seed=m + n)
+    rng = np.random.default_rng(5)
+    r = 32
+    u = (rng.standard_normal((m, r)) * 4).astype(np.float32)
+    l2 = wl.bf16_to_f32(wl.f32_to_bf16_bits(rng.normal(0, 0.02, (r, n)).astype(np.float32)))
+    y = mxq.gemm(gu.qtensor_from_oracle(qa, m, k), gu.qtensor_from_oracle(qw, n, k),
+                 u=gu.to_dev_f32(u),
+                 l2t=gu.to_dev_bf16(wl.f32_to_bf16_bits(np.ascontiguousarray(l2.T))))
+    a_deq = np.hstack([gu.dequant_a_for_gemm(qa), u.astype(np.float64)])
+    w_deq = np.hstack([gu.dequant_w_for_gemm(qw), l2.T.astype(np.float64)])
+    ratio = gu.check_gemm(y, a_deq, w_deq, 1.0, tag=f"mx tiles {m}x{n}x{k}")
+    gu.say(f"  worst err/tol {ratio:.3g}")
