@@ -218,7 +218,8 @@ static hipError_t gemm_launch(const mxq_qtensor* a, const mxq_qtensor* w, const 
   // exactly to 16-bit operands (E4M3 MFMA products are not summed to fp32
   // accuracy on this hardware)
   if (a->fmt == MXQ_FMT_MXFP4 && w->fmt == MXQ_FMT_MXFP4) return launch_gemm_mx(g, s);
-  return launch_gemm_dq(g, s);
+  if (w->fmt == MXQ_FMT_INT4) return launch_gemm_dq(g, s);
+  return launch_gemm_dqp(g, s);
 }
 
 mxq_status mxq_gemm(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* w_out_col,

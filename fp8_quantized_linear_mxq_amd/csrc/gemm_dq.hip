@@ -1,24 +1,13 @@
-// GEMM routes on exact 16-bit dequantization: every (activation, weight)
-// format pair except MXFP4 x MXFP4 (which runs on the scaled MFMA directly).
+// GEMM route for INT4 weight rows (Chameleon palette: symmetric int4 with an
+// fp32 scale per 32), against MXFP8, NVFP4 or MXFP4 activations.
 //
-// Why dequantize: on gfx950 every MFMA that takes E4M3 operands keeps only
-// about 15 bits below the largest product of its dot product (measured: the
-// error reaches 2**-11 of the largest product), which cannot meet the layer's
-// 1e-5 * sum|a w| bound on heavy-tailed activations; the 16-bit MFMAs round
-// like fp32 and E2M1 x E2M1 on the scaled MFMA is exact.  Every code/scale
-// pair used here dequantizes exactly into a 16-bit float:
-//   E2M1 x E4M3 block scale (NVFP4)  <= 6 significant bits, in [2**-10, 2688]
-//   E4M3 x E8M0 (MXFP8), E2M1 x E8M0 (MXFP4)  <= 4 significant bits
-// so NVFP4 x NVFP4 runs on the fp16 MFMA (one hardware FP4->fp16 convert and
-// one packed fp16 multiply per two elements) and everything else on the bf16
-// MFMA (E8M0 exponents need bf16's range; the hardware converts apply an
-// E8M0 scale exactly).  NVFP4 tensor scales are applied in the epilogue.
-//
-// INT4 weight rows (Chameleon palette: symmetric int4 with an fp32 scale per
-// 32) cannot fold their arbitrary fp32 scale into a 16-bit operand, so each
+// The arbitrary fp32 weight scale cannot fold into a 16-bit operand, so each
 // 32-element block's partial sum comes from two bf16 MFMAs on the integer
 // codes (exact in bf16) and is scaled into an fp32 accumulator with one FMA
-// per output element.
+// per output element.  Activations are dequantized exactly to 16-bit (see
+// gemm_dqp.hip for why the E4M3 MFMAs are not used): E4M3 x E8M0 and
+// E2M1 x E8M0 have <= 4 significant bits, E2M1 x E4M3 (NVFP4) <= 6 bits;
+// NVFP4 tensor scales are applied in the epilogue.
 //
 // Tile 128x128, K-tile 64, 2x2 waves of 64x64, 32x32x16 MFMAs; operands are
 // dequantized while being stored to LDS, so each element is converted once
@@ -348,232 +337,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
 }
 
 
-// ---------------------------------------------------------------------------
-// Register-dequantizing kernel for MX/NVFP4 weights (v2).
-//
-// LDS holds the raw codes (4x smaller than 16-bit tiles), and each wave
-// dequantizes its own MFMA fragments in registers.  Inside a 128-wide K-tile
-// the reduction index is permuted consistently for both operands: lane half
-// h supplies K = 64h + 8ks + [0, 8) at MFMA step ks, so each lane's
-// fragments for the whole K-tile are one contiguous 64-byte (E4M3) or
-// 32-byte (E2M1) run of its row -- a few 16-byte LDS reads -- and every
-// fragment still lies inside a single 16/32-element scale block.  A sum's
-// terms are only reordered, so the value computed is unchanged.  The lane's
-// block-scale bytes for the tile are one 16/32-bit global load.
-// ---------------------------------------------------------------------------
-
-constexpr int BK2 = 128;
-constexpr int kSlab2 = 8;   // K-tiles (8 MFMA steps each) per fp32 slab
-
-__device__ __forceinline__ float e8m0_scale(uint32_t code) {
-  // E8M0 as an fp32 power of two for the hardware converts; code 0 (2**-127,
-  // an fp32 subnormal the converts do not apply exactly) is taken as 2**-126
-  return __uint_as_float((code == 0 ? 1u : code) << 23);
-}
-
-template <int K>
-struct OpBytes { static constexpr int v = (K == K_MX8) ? 128 : 64; };
-
-// Dequantize fragment ks (8 elements) of a lane's raw run into 16-bit values.
-template <int K, bool FP16>
-__device__ __forceinline__ uint4 dq_frag(const uint32_t* raw, int ks, uint32_t sc) {
-  if constexpr (K == K_MX8) {
-    const float s = e8m0_scale((sc >> (8 * (ks >> 2))) & 0xFFu);
-    const uint32_t d0 = raw[2 * ks], d1 = raw[2 * ks + 1];
-    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, s, false)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, s, true)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, s, false)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, s, true)));
-  } else if constexpr (K == K_MX4) {
-    const float s = e8m0_scale((sc >> (8 * (ks >> 2))) & 0xFFu);
-    const uint32_t d = raw[ks];
-    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 0)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 1)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 2)),
-                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 3)));
-  } else {  // NVFP4: E4M3 scale per 16 = per two fragments
-    const float s = e4m3_value((sc >> (8 * (ks >> 1))) & 0xFFu);
-    const uint32_t d = raw[ks];
-    if constexpr (FP16) {
-      const v2h sh = {(_Float16)s, (_Float16)s};
-      return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sh),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sh),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sh),
-                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sh));
-    } else {
-      const v2f f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
-      const v2f f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
-      const v2f f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
-      const v2f f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
-      return make_uint4(pack_hi16(f0.x * s, f0.y * s), pack_hi16(f1.x * s, f1.y * s),
-                        pack_hi16(f2.x * s, f2.y * s), pack_hi16(f3.x * s, f3.y * s));
-    }
-  }
-}
-
-// The lane's scale bits for one K-tile: MX 2 bytes (blocks 2h, 2h+1), NVFP4
-// 4 bytes (16-blocks 4h..4h+3).
-template <int K>
-__device__ __forceinline__ uint32_t load_scales(const uint8_t* row, int kt, int half) {
-  if constexpr (K == K_NV) return *reinterpret_cast<const uint32_t*>(row + kt * 8 + half * 4);
-  else return *reinterpret_cast<const uint16_t*>(row + kt * 4 + half * 2);
-}
-
-template <int AK, int WK, bool LR>
-__global__ __launch_bounds__(kThreads, 2) void gemm_dq2_kernel(DqParams dp) {
-  const GemmP& p = dp.g;
-  constexpr bool FP16 = (AK == K_NV && WK == K_NV);
-  constexpr int A_RB = OpBytes<AK>::v, W_RB = OpBytes<WK>::v;
-  constexpr int A_CH = A_RB / 16, W_CH = W_RB / 16;
-  constexpr int A_LOADS = BM * A_CH / kThreads, W_LOADS = BN * W_CH / kThreads;
-  constexpr int A_DW = A_RB / 8, W_DW = W_RB / 8;   // dwords per lane run (half a row slice)
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * A_RB];
-  __shared__ __attribute__((aligned(16))) uint8_t sW[2][BN * W_RB];
-
-  const int tile = remap_tile(blockIdx.x, p.tiles_m * p.tiles_n);
-  const int m0 = (tile / p.tiles_n) * BM, n0 = (tile % p.tiles_n) * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, half = lane >> 5;
-  const int KT = p.K / BK2;
-
-  const uint8_t* ga[A_LOADS];
-  int la[A_LOADS];
-  bool va[A_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int q = tid + i * kThreads, r = q / A_CH, c = q % A_CH;
-    va[i] = (m0 + r) < p.M;
-    ga[i] = p.a + (int64_t)(va[i] ? m0 + r : 0) * p.lda + c * 16;
-    la[i] = r * A_RB + ((c ^ swz<A_CH>(r)) * 16);
-  }
-  const uint8_t* gw[W_LOADS];
-  int lw[W_LOADS];
-  bool vw[W_LOADS];
-#pragma unroll
-  for (int i = 0; i < W_LOADS; ++i) {
-    const int q = tid + i * kThreads, r = q / W_CH, c = q % W_CH;
-    vw[i] = (n0 + r) < p.N;
-    gw[i] = p.w + (int64_t)(vw[i] ? n0 + r : 0) * p.ldw + c * 16;
-    lw[i] = r * W_RB + ((c ^ swz<W_CH>(r)) * 16);
-  }
-  const uint8_t* sa_row[2];
-  const uint8_t* sw_row[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = m0 + wm * 64 + i * 32 + l32;
-    sa_row[i] = p.as + (int64_t)(r < p.M ? r : p.M - 1) * p.ldas;
-    const int c = n0 + wn * 64 + i * 32 + l32;
-    sw_row[i] = p.ws + (int64_t)(c < p.N ? c : p.N - 1) * p.ldws;
-  }
-
-  uint4 ra[A_LOADS], rw[W_LOADS];
-  uint32_t sa[2], sw[2], nsa[2], nsw[2];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      ra[i] = va[i] ? *reinterpret_cast<const uint4*>(ga[i] + (int64_t)kt * A_RB) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < W_LOADS; ++i)
-      rw[i] = vw[i] ? *reinterpret_cast<const uint4*>(gw[i] + (int64_t)kt * W_RB) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      nsa[i] = load_scales<AK>(sa_row[i], kt, half);
-      nsw[i] = load_scales<WK>(sw_row[i], kt, half);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) *reinterpret_cast<uint4*>(&sA[buf][la[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < W_LOADS; ++i) *reinterpret_cast<uint4*>(&sW[buf][lw[i]]) = rw[i];
-  };
-
-  v16f acc[2][2], tot[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[i][j] = v16f{};
-      tot[i][j] = v16f{};
-    }
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) { sa[i] = nsa[i]; sw[i] = nsw[i]; }
-    if (kt + 1 < KT) gload(kt + 1);
-    // this lane's raw runs: half h holds bytes [h * RB/2, (h+1) * RB/2) of its row slice
-    uint32_t araw[2][A_DW], wraw[2][W_DW];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = wm * 64 + i * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < A_DW / 4; ++t) {
-        const int c = half * (A_CH / 2) + t;
-        const uint4 v = *reinterpret_cast<const uint4*>(&sA[buf][r * A_RB + ((c ^ swz<A_CH>(r)) * 16)]);
-        araw[i][4 * t] = v.x; araw[i][4 * t + 1] = v.y; araw[i][4 * t + 2] = v.z; araw[i][4 * t + 3] = v.w;
-      }
-      const int rb = wn * 64 + i * 32 + l32;
-#pragma unroll
-      for (int t = 0; t < W_DW / 4; ++t) {
-        const int c = half * (W_CH / 2) + t;
-        const uint4 v = *reinterpret_cast<const uint4*>(&sW[buf][rb * W_RB + ((c ^ swz<W_CH>(rb)) * 16)]);
-        wraw[i][4 * t] = v.x; wraw[i][4 * t + 1] = v.y; wraw[i][4 * t + 2] = v.z; wraw[i][4 * t + 3] = v.w;
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < BK2 / 16; ++ks) {
-      uint4 af[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        af[i] = dq_frag<AK, FP16>(araw[i], ks, sa[i]);
-        bf[i] = dq_frag<WK, FP16>(wraw[i], ks, sw[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          if constexpr (FP16)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                __builtin_bit_cast(v8h, af[i]), __builtin_bit_cast(v8h, bf[j]), acc[i][j], 0, 0, 0);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(v8bf, af[i]), __builtin_bit_cast(v8bf, bf[j]), acc[i][j], 0, 0, 0);
-        }
-    }
-    if ((kt + 1) % kSlab2 == 0) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          tot[i][j] += acc[i][j];
-          acc[i][j] = v16f{};
-        }
-    }
-    if (kt + 1 < KT) lstore(buf ^ 1);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] += tot[i][j];
-  float alpha = 1.0f;
-  if constexpr (AK == K_NV) alpha *= *dp.a_gp;
-  if constexpr (WK == K_NV) alpha *= *dp.w_gp;
-  epilogue<LR>(p, acc, alpha, m0, n0, wm, wn, lane);
-}
-
-template <int AK, int WK>
-hipError_t dispatch2(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
-  if (lr) gemm_dq2_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
-  else gemm_dq2_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
-  return hipGetLastError();
-}
-
 template <int AK, int WK>
 hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
   if (lr) gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
@@ -583,12 +346,8 @@ hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
 
 template <int AK>
 hipError_t dispatch_w(int w_fmt, bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
-  switch (w_fmt) {
-    case FMT_NVFP4: return dispatch2<AK, K_NV>(lr, grid, p, s);
-    case FMT_MXFP4: return dispatch2<AK, K_MX4>(lr, grid, p, s);
-    case FMT_INT4: return dispatch<AK, K_I4>(lr, grid, p, s);
-    default: return hipErrorInvalidValue;
-  }
+  if (w_fmt != FMT_INT4) return hipErrorInvalidValue;   // MX/NVFP4 weights: gemm_dqp.hip
+  return dispatch<AK, K_I4>(lr, grid, p, s);
 }
 
 }  // namespace

@@ -1,0 +1,383 @@
+// Pipelined exact-dequant GEMM for MX/NVFP4 weights: every (activation,
+// weight) pair with A in {MXFP8, NVFP4, MXFP4} and W in {MXFP4, NVFP4} except
+// MXFP4 x MXFP4, which has its own scaled-MFMA kernel.
+//
+// Arithmetic (why 16-bit): on gfx950 the MFMAs that take E4M3 operands keep
+// only about 15 bits below the largest product of each dot product, which
+// cannot meet the layer's 1e-5 * sum|a w| bound on heavy-tailed activations,
+// while the 16-bit MFMAs round like fp32.  Each code times its block scale is
+// exact in a 16-bit float: E4M3 x E8M0 and E2M1 x E8M0 have <= 4 significant
+// bits (bf16 for the E8M0 range), E2M1 x E4M3 (NVFP4) <= 6 bits within
+// [2**-10, 2688] (fp16 when both operands are NVFP4, bf16 otherwise).  NVFP4
+// tensor scales multiply the accumulator in the epilogue.
+//
+// Organisation (the same pipeline as the MXFP4 kernel):
+//  * workgroup tile 256 x (64*TN), four waves in a 2 x 2 grid, each wave
+//    128 x (32*TN): every dequantized fragment feeds TN (activation) or 4
+//    (weight) MFMAs;
+//  * raw code and scale tiles (4-bit codes are a quarter, 8-bit codes half
+//    the bytes of 16-bit tiles) stream into a 3-stage LDS ring with direct
+//    global->LDS loads two K-tiles ahead of the MFMAs;
+//  * inside a 128-wide K-tile the reduction index is permuted identically for
+//    both operands: lane half h supplies K = 64h + 8ks + [0, 8) at MFMA step
+//    ks, so a lane's fragments for the whole K-tile are one contiguous run of
+//    its row (2-4 16-byte LDS reads) and every fragment lies in one scale
+//    block; the sum's terms are only reordered;
+//  * a step reads its K-tile's activation runs one 16-byte chunk ahead of
+//    the MFMAs that use them (few registers, so 128-row wave tiles fit); the
+//    loop is branch-free (tiles past the end of K load as zeros);
+//  * the MFMAs compute D^T = W A^T and the output leaves through LDS as
+//    16-byte pieces of whole rows.
+#include "device_common.h"
+#include "gemm_common.h"
+#include "gemm_pipe.h"
+#include "kernels.h"
+
+namespace mxq {
+namespace {
+
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+enum : int { K_NV = 0, K_MX8 = 1, K_MX4 = 2 };
+
+constexpr int BK = 128;
+constexpr int kSlab = 8;   // K-tiles (8 MFMA steps each) per fp32 slab when slabbing
+
+template <int K> constexpr int row_bytes() { return K == K_MX8 ? 128 : 64; }
+template <int K> constexpr int scale_bytes() { return K == K_NV ? 8 : 4; }
+
+struct DqpParams {
+  GemmP g;
+  const float* a_gp;   // NVFP4 tensor scale of a
+  const float* w_gp;   // NVFP4 tensor scale of w
+  int gm;              // tile-rows per group of the tile order
+};
+
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+__device__ __forceinline__ float e8m0_scale(uint32_t code) {
+  // E8M0 as an fp32 power of two for the hardware converts; code 0 (2**-127,
+  // an fp32 subnormal the converts do not apply exactly) is taken as 2**-126
+  return __uint_as_float((code == 0 ? 1u : code) << 23);
+}
+
+// The lane's block scales of a K-tile, one value per group of MFMA steps:
+// MX: steps 0-3 and 4-7 (two 32-blocks), NVFP4: steps 2q, 2q+1 (16-blocks).
+template <int K, bool FP16>
+struct Scales {
+  float s[K == K_NV ? 4 : 2];
+};
+
+template <int K, bool FP16>
+__device__ __forceinline__ Scales<K, FP16> lane_scales(uint32_t dw, int half) {
+  Scales<K, FP16> r;
+  if constexpr (K == K_NV) {
+    // dword `half` of the row's 8 scale bytes: 16-blocks 4h .. 4h+3
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r.s[q] = e4m3_value((dw >> (8 * q)) & 0xFFu);
+  } else {
+    // bytes 2h, 2h+1 of the row's 4 scale bytes: 32-blocks 2h, 2h+1
+    const uint32_t b = dw >> (16 * half);
+    r.s[0] = e8m0_scale(b & 0xFFu);
+    r.s[1] = e8m0_scale((b >> 8) & 0xFFu);
+  }
+  return r;
+}
+
+// Dequantize MFMA step ks (8 elements) of a lane's raw run to 16-bit values.
+template <int K, bool FP16>
+__device__ __forceinline__ uint4 dq(const uint32_t* raw, int ks, const Scales<K, FP16>& sc) {
+  if constexpr (K == K_MX8) {
+    const float s = sc.s[ks >> 2];
+    const uint32_t d0 = raw[2 * ks], d1 = raw[2 * ks + 1];
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, s, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, s, true)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, s, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d1, s, true)));
+  } else if constexpr (K == K_MX4) {
+    const float s = sc.s[ks >> 2];
+    const uint32_t d = raw[ks];
+    return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 0)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 2)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, s, 3)));
+  } else {
+    const float s = sc.s[ks >> 1];
+    const uint32_t d = raw[ks];
+    if constexpr (FP16) {
+      const v2h sh = {(_Float16)s, (_Float16)s};
+      return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * sh),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * sh),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * sh),
+                        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * sh));
+    } else {
+      // products of <= 6 significant bits: truncating the fp32 product to
+      // its top 16 bits is exact
+      const v2f f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+      const v2f f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+      const v2f f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+      const v2f f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+      return make_uint4(pack_hi16(f0.x * s, f0.y * s), pack_hi16(f1.x * s, f1.y * s),
+                        pack_hi16(f2.x * s, f2.y * s), pack_hi16(f3.x * s, f3.y * s));
+    }
+  }
+}
+
+template <int AK, int WK, int TM, int TN, bool SLAB, bool LR>
+__global__ __launch_bounds__(kThreads, 1) void gemm_dqp_kernel(DqpParams dp) {
+  const GemmP& p = dp.g;
+  constexpr bool FP16 = (AK == K_NV && WK == K_NV);
+  constexpr int TBM = 64 * TM, TBN = 64 * TN;
+  constexpr int A_RB = row_bytes<AK>(), W_RB = row_bytes<WK>();
+  constexpr int A_CH = A_RB / 16, W_CH = W_RB / 16;
+  constexpr int SBA = scale_bytes<AK>(), SBW = scale_bytes<WK>();
+  constexpr int A_STAGE = TBM * A_RB, W_STAGE = TBN * W_RB;
+  constexpr int S_STAGE = scale_region_bytes<TBM, SBA, TBN, SBW>();
+  constexpr int STAGE = A_STAGE + W_STAGE + S_STAGE;
+  constexpr int NT = (TBM * A_CH + TBN * W_CH) / 256 + S_STAGE / 1024;   // loads per wave per K-tile
+  constexpr int A_DW = A_RB / 8, W_DW = W_RB / 8;   // dwords of a lane's run per K-tile
+  static_assert(2 * NT < 64, "vmcnt range");
+  // three separate arrays: reads of one stage are visibly independent of the
+  // loads in flight into the others, so the compiler adds no wait for them
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, dp.gm, tm, tn);
+  const int m0 = tm * TBM, n0 = tn * TBN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int KT = p.K / BK;
+
+  // byte offsets within a stage of this lane's fragment and scale reads
+  uint32_t a_off[TM][A_DW / 4], w_off[TN][W_DW / 4], sa_off[TM], sw_off[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * 32 * TM + i * 32 + l32;
+#pragma unroll
+    for (int t = 0; t < A_DW / 4; ++t) {
+      const int c = half * (A_CH / 2) + t;
+      a_off[i][t] = r * A_RB + ((c ^ swz<A_CH>(r)) * 16);
+    }
+    sa_off[i] = A_STAGE + W_STAGE + r * SBA + (SBA == 8 ? 4 * half : 0);
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int r = wn * 32 * TN + j * 32 + l32;
+#pragma unroll
+    for (int t = 0; t < W_DW / 4; ++t) {
+      const int c = half * (W_CH / 2) + t;
+      w_off[j][t] = A_STAGE + r * W_RB + ((c ^ swz<W_CH>(r)) * 16);
+    }
+    sw_off[j] = A_STAGE + W_STAGE + TBM * SBA + r * SBW + (SBW == 8 ? 4 * half : 0);
+  }
+
+  auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
+    const bool past = kt >= KT;   // past the end of K: a tile of zeros
+    kt = past ? KT - 1 : kt;
+    issue_tile<TBM, A_RB>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past);
+    issue_tile<TBN, W_RB>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past);
+    issue_scale_tile<TBM, SBA, TBN, SBW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane, past);
+  };
+
+  v16f acc[TM][TN];
+  v16f tot[SLAB ? TM : 1][SLAB ? TN : 1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = v16f{};
+  if constexpr (SLAB) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) tot[i][j] = v16f{};
+  }
+
+  // Dequantize and multiply the K-tile in stage `st`.  The weight runs and
+  // all scales are read up front; the activation runs are read one 16-byte
+  // chunk (A_KS MFMA steps) ahead of their use, so only two chunks per row
+  // tile are ever held in registers.
+  constexpr int A_NC = A_DW / 4;          // 16-byte chunks per lane run
+  constexpr int A_KS = (BK / 16) / A_NC;  // MFMA steps per chunk
+  auto compute = [&](const uint8_t* st) __attribute__((always_inline)) {
+    uint32_t wraw[TN][W_DW];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int t = 0; t < W_DW / 4; ++t) {
+        const uint4 v = *reinterpret_cast<const uint4*>(st + w_off[j][t]);
+        wraw[j][4 * t] = v.x; wraw[j][4 * t + 1] = v.y; wraw[j][4 * t + 2] = v.z; wraw[j][4 * t + 3] = v.w;
+      }
+    Scales<AK, FP16> sa[TM];
+    Scales<WK, FP16> sw[TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      sa[i] = lane_scales<AK, FP16>(*reinterpret_cast<const uint32_t*>(st + sa_off[i]), half);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      sw[j] = lane_scales<WK, FP16>(*reinterpret_cast<const uint32_t*>(st + sw_off[j]), half);
+    uint4 ach[2][TM];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) ach[0][i] = *reinterpret_cast<const uint4*>(st + a_off[i][0]);
+#pragma unroll
+    for (int c = 0; c < A_NC; ++c) {
+      if (c + 1 < A_NC) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) ach[(c + 1) & 1][i] = *reinterpret_cast<const uint4*>(st + a_off[i][c + 1]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < A_KS; ++kk) {
+        const int ks = c * A_KS + kk;
+        uint4 af[TM], bf[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          // the chunk's dwords sit at run positions 4c .. 4c+3
+          uint32_t run[A_DW];
+          const uint4 v = ach[c & 1][i];
+          run[4 * c] = v.x; run[4 * c + 1] = v.y; run[4 * c + 2] = v.z; run[4 * c + 3] = v.w;
+          af[i] = dq<AK, FP16>(run, ks, sa[i]);
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[j] = dq<WK, FP16>(wraw[j], ks, sw[j]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (FP16)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  __builtin_bit_cast(v8h, bf[j]), __builtin_bit_cast(v8h, af[i]), acc[i][j], 0, 0, 0);
+            else
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(v8bf, bf[j]), __builtin_bit_cast(v8bf, af[i]), acc[i][j], 0, 0, 0);
+          }
+      }
+    }
+  };
+
+  // One K-tile (tile t lives in stage t % 3): wait until K-tile kt has landed
+  // (kt+1 may still be in flight) and this wave's reads are complete, then
+  // barrier (every wave is done with stage (kt-1) % 3), load K-tile kt+2
+  // into that stage, and dequantize and multiply K-tile kt from its stage.
+  auto step = [&](int kt, const uint8_t* st_cur, uint8_t* st_load) __attribute__((always_inline)) {
+    wait_vmcnt<NT>();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 2, st_load);
+    compute(st_cur);
+    if constexpr (SLAB) {
+      if (kt < KT && (kt + 1) % kSlab == 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            tot[i][j] += acc[i][j];
+            acc[i][j] = v16f{};
+          }
+      }
+    }
+  };
+
+  // the loop runs a whole number of 3-step groups with no branch (keeping the
+  // accumulators in place); K-tiles past the end are loaded as zeros
+  issue(0, st0);
+  issue(1, st1);
+  for (int kt = 0; kt < KT; kt += 3) {
+    step(kt, st0, st2);
+    step(kt + 1, st1, st0);
+    step(kt + 2, st2, st1);
+  }
+  wait_vmcnt<0>();   // the zero loads issued past the end
+  if constexpr (SLAB) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] += tot[i][j];
+  }
+  float alpha = 1.0f;
+  if constexpr (AK == K_NV) alpha *= *dp.a_gp;
+  if constexpr (WK == K_NV) alpha *= *dp.w_gp;
+  wait_lgkmcnt0();
+  __syncthreads();
+  static_assert(2 * 32 * (TN * 64 + 16) <= STAGE, "two staging slices per stage");
+  uint8_t* region = (wave < 2 ? st0 : st1) + (wave & 1) * 32 * (TN * 64 + 16);
+  epilogue_tr<LR, TM, TN>(p, acc, alpha, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
+}
+
+template <int AK, int WK, int TM, int TN, bool SLAB>
+hipError_t launch_cfg(bool lr, DqpParams dp, hipStream_t s) {
+  dp.g.tiles_m = (dp.g.M + 64 * TM - 1) / (64 * TM);
+  dp.g.tiles_n = (dp.g.N + 64 * TN - 1) / (64 * TN);
+  const int tiles = dp.g.tiles_m * dp.g.tiles_n;
+  // tile-rows per group: one XCD's share (tiles / 8) as a near-square block
+  dp.gm = 1;
+  while (dp.gm * 2 <= dp.g.tiles_m && dp.gm * 2 * dp.gm * 2 <= (tiles + 7) / 8) dp.gm *= 2;
+  const dim3 grid(tiles);
+  if (lr) gemm_dqp_kernel<AK, WK, TM, TN, SLAB, true><<<grid, kThreads, 0, s>>>(dp);
+  else gemm_dqp_kernel<AK, WK, TM, TN, SLAB, false><<<grid, kThreads, 0, s>>>(dp);
+  return hipGetLastError();
+}
+
+template <int AK, int WK>
+hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
+  const int64_t M = dp.g.M, N = dp.g.N;
+  // past 32 K-tiles the fp32 chains are flushed into a second accumulator,
+  // which only the small tile has the registers for
+  if (dp.g.K / BK > 4 * kSlab) return launch_cfg<AK, WK, 2, 2, true>(lr, dp, s);
+  // Short K (under 16 K-tiles): 128x128 tiles, two workgroups per compute
+  // unit, so one tile's pipeline fill and output stores overlap the other's
+  // MFMAs.  Longer K: the 256-row tile that fills the 256 compute units in
+  // the fewest rounds per unit of work (fewest dequantizations per MFMA);
+  // ties go to 256 x 192.
+  if (dp.g.K / BK < 16) return launch_cfg<AK, WK, 2, 2, false>(lr, dp, s);
+  const int64_t cu = 256;
+  auto rounds = [&](int64_t tbm, int64_t tbn) {
+    const int64_t t = ((M + tbm - 1) / tbm) * ((N + tbn - 1) / tbn);
+    return (t + cu - 1) / cu;
+  };
+  const int64_t c3 = rounds(256, 192) * 12, c2 = rounds(256, 128) * 8;
+  if constexpr (AK != K_MX8) {
+    const int64_t c4 = rounds(256, 256) * 16;
+    if (c4 < c3 && c4 <= c2) return launch_cfg<AK, WK, 4, 4, false>(lr, dp, s);
+  }
+  if (c3 <= c2) return launch_cfg<AK, WK, 4, 3, false>(lr, dp, s);
+  return launch_cfg<AK, WK, 4, 2, false>(lr, dp, s);
+}
+
+template <int AK>
+hipError_t launch_w(int w_fmt, bool lr, const DqpParams& dp, hipStream_t s) {
+  if (w_fmt == FMT_NVFP4) return launch_pair<AK, K_NV>(lr, dp, s);
+  return launch_pair<AK, K_MX4>(lr, dp, s);
+}
+
+}  // namespace
+
+hipError_t launch_gemm_dqp(const GemmArgs& a, hipStream_t s) {
+  DqpParams dp;
+  GemmP& p = dp.g;
+  p.a = a.a_codes; p.lda = a.lda; p.as = a.a_scales; p.ldas = a.ld_as;
+  p.w = a.w_codes; p.ldw = a.ldw; p.ws = a.w_scales; p.ldws = a.ld_ws;
+  p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K;
+  p.tiles_m = p.tiles_n = 0;
+  p.col_map = a.col_map;
+  p.u = a.u; p.ld_u = a.ld_u; p.l2t = a.l2t; p.rank = a.rank;
+  p.bias = a.bias;
+  p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
+  dp.a_gp = a.a_g;
+  dp.w_gp = a.w_g;
+  const bool lr = a.rank > 0;
+  if (a.w_fmt != FMT_NVFP4 && a.w_fmt != FMT_MXFP4) return hipErrorInvalidValue;
+  switch (a.a_fmt) {
+    case FMT_NVFP4: return launch_w<K_NV>(a.w_fmt, lr, dp, s);
+    case FMT_MXFP8: return launch_w<K_MX8>(a.w_fmt, lr, dp, s);
+    case FMT_MXFP4: return launch_w<K_MX4>(a.w_fmt, lr, dp, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mxq

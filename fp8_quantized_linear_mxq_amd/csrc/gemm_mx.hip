@@ -41,12 +41,6 @@ constexpr int RB = BK / 2;        // bytes per row per K-tile (E2M1)
 constexpr int CH = RB / 16;       // 16-byte chunks per row
 constexpr int kSlab = 16;         // K-tiles per fp32 slab when slabbing
 
-}  // namespace
-
-__device__ uint8_t g_zero16[16];
-
-namespace {
-
 template <int TM, int TN, bool SLAB, bool LR>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
   constexpr int TBM = 64 * TM, TBN = 64 * TN;
@@ -85,7 +79,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
     sw_off[j] = A_STAGE + W_STAGE + (TBM + r) * 4;
   }
 
-  auto issue = [&](int kt, uint8_t* st) {
+  auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const bool past = kt >= KT;   // past the end of K: a tile of zeros
     kt = past ? KT - 1 : kt;
     issue_tile<TBM, RB>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past);
@@ -96,7 +90,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
     v4i a[TM][2], w[TN][2];
     uint32_t sa[TM], sw[TN];
   };
-  auto read = [&](const uint8_t* st, Frag& f) {
+  auto read = [&](const uint8_t* st, Frag& f) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -124,7 +118,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
       for (int j = 0; j < TN; ++j) tot[i][j] = v16f{};
   }
 
-  auto compute = [&](const Frag& f) {
+  auto compute = [&](const Frag& f) __attribute__((always_inline)) {
     // the lane's E8M0 bytes for K-blocks 2s + half sit at byte 2s after the shift
     uint32_t sa[TM], sw[TN];
 #pragma unroll
@@ -163,7 +157,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
   // past the end are loaded as zeros and add nothing.
   constexpr int N_MFMA = 2 * TM * TN;
   constexpr int N_DS = 2 * (TM + TN) + TM + TN;
-  auto step = [&](int kt, const uint8_t* st_next, uint8_t* st_cur, const Frag& cur, Frag& nxt) {
+  auto step = [&](int kt, const uint8_t* st_next, uint8_t* st_cur, const Frag& cur, Frag& nxt) __attribute__((always_inline)) {
     wait_vmcnt<NT>();
     wait_lgkmcnt0();
     __builtin_amdgcn_s_barrier();
@@ -251,7 +245,7 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
   // Large tiles move the fewest bytes per MFMA; pick the one whose tile count
   // fills the 256 compute units in the fewest rounds, per unit of tile work.
   const int64_t cu = 256;
-  auto rounds = [&](int tbm, int tbn) {
+  auto rounds = [&](int tbm, int tbn) __attribute__((always_inline)) {
     const int64_t t = ((a.M + tbm - 1) / tbm) * ((a.N + tbn - 1) / tbn);
     return (t + cu - 1) / cu;
   };

@@ -20,9 +20,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// 16 zero bytes: the source of every load of a K-tile past the end of K, so
-// such a tile multiplies to exactly zero and the main loop needs no branch.
-extern __device__ uint8_t g_zero16[16];
+// 16 zero bytes (one copy per code object): the source of every load of a
+// K-tile past the end of K, so such a tile multiplies to exactly zero and the
+// main loop needs no branch.
+static __device__ uint8_t g_zero16[16];
 
 // Direct loads of one operand tile (ROWS rows x RB bytes of K-tile kt) into
 // an LDS stage.  The 4 waves split the tile into 64-lane instructions; slot L

@@ -53,6 +53,7 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_dqp(const GemmArgs& a, hipStream_t s);
 
 struct SelectArgs {
   const void* w; int dtype;

@@ -121,3 +121,26 @@ def test_gemm_mx_tiles(m, n, k):
     w_deq = np.hstack([gu.dequant_w_for_gemm(qw), l2.T.astype(np.float64)])
     ratio = gu.check_gemm(y, a_deq, w_deq, 1.0, tag=f"mx tiles {m}x{n}x{k}")
     gu.say(f"  worst err/tol {ratio:.3g}")
+
+
+# Long-K shapes that make the dequantizing route pick its 256-row workgroup
+# tiles (256x128; 256x192; 256x256 for 4-bit activations, 256x128 for 8-bit),
+# with ragged M and N tails; output rows are checked on a sample.
+DQ_TILE_SHAPES = [(2000, 2300, 2048), (4000, 2300, 2048), (4000, 4000, 2048)]
+DQ_PAIRS = [(a, w) for a in ("MXFP8", "NVFP4", "MXFP4") for w in ("MXFP4", "NVFP4")
+            if (a, w) != ("MXFP4", "MXFP4")]
+
+
+@pytest.mark.parametrize("m,n,k", DQ_TILE_SHAPES)
+@pytest.mark.parametrize("fa,fw", DQ_PAIRS)
+def test_gemm_dq_tiles(fa, fw, m, n, k):
+    import fp8_quantized_linear_mxq_amd as mxq
+    gu.say(f"gemm {fa}x{fw} tiles M={m} N={n} K={k}")
+    qa, qw = _operands(m, n, k, fa, fw, seed=m + 3 * n + len(fa + fw))
+    y = mxq.gemm(gu.qtensor_from_oracle(qa, m, k), gu.qtensor_from_oracle(qw, n, k))
+    rng = np.random.default_rng(m + n)
+    rows = np.unique(np.concatenate([rng.choice(m, 96, replace=False), [0, 255, 256, m - 1]]))
+    a_deq = gu.dequant_a_for_gemm(qa)[rows]
+    ratio = gu.check_gemm(y, a_deq, gu.dequant_w_for_gemm(qw), gu.alpha_of(qa, qw), rows=rows,
+                          tag=f"{fa}x{fw} tiles {m}x{n}x{k}")
+    gu.say(f"  worst err/tol {ratio:.3g}")
