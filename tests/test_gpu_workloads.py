@@ -92,8 +92,10 @@ def test_linear_workload(name):
 
 def test_select_and_mixed_conv():
     """Per-channel format choice on the full 1280 x 23040 convolution weight,
-    then the grouped GEMM on MXFP8 activations of a reduced latent (24 x 24,
-    same 2560 channels, so K is the full 23040)."""
+    then the grouped GEMM on MXFP8 activations of the full 128 x 128 x 2560
+    latent (im2col M = 16384, K = 23040, 755 MB of bf16), codes and outputs
+    checked on sampled rows (row 0 is a corner pixel: its padding taps are
+    all-zero blocks)."""
     import torch
     import fp8_quantized_linear_mxq_amd as mxq
     w = wl.WORKLOADS["chameleon_conv"]
@@ -106,9 +108,10 @@ def test_select_and_mixed_conv():
     _check_selection(choice, sse, perm, counts, c_ref, sse_ref, perm_ref)
     assert float(g.cpu()[0]) == float(oq.nvfp4_tensor_scale(wt))
 
-    gu.say("conv workload: grouped GEMM on a 24x24 latent")
-    lat = wl.conv_latent(w, hw=(24, 24))
+    gu.say("conv workload: grouped GEMM on the full latent")
+    lat = wl.conv_latent(w)
     act = wl.im2col(lat)
+    del lat
     _mixed_gemm_check(act, wt, choice, perm, counts, g, tag="conv")
 
 
@@ -184,5 +187,6 @@ def _mixed_gemm_check(act_bits, wt, choice, perm, counts, g, tag):
         _check_codes(groups[ci], name, qw_ref, tag=f"{tag} weights {name}")
         w_deq = oq.dequantize(qw_ref)       # tensor scale included: alpha = g_w on the GPU
         r = gu.check_gemm(y, a_deq, w_deq, 1.0, rows=rows, cols=idx, tag=f"{tag} {name}")
+        gu.say(f"  {tag} {name}: {len(idx)} rows, worst err/tol {r:.3g}")
         worst = max(worst, r)
     gu.say(f"  {tag}: worst err/tol {worst:.3g}, groups {cnt.tolist()}")
