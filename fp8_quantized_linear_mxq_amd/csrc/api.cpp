@@ -144,10 +144,9 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
   a.tensor_scale_out = out->tensor_scale;
   a.static_tensor_scale = static_tensor_scale;
   a.partials = static_cast<float*>(workspace);
-  hipError_t e = launch_quantize(a, as_stream(stream));
-  if (e != hipSuccess) return MXQ_ERR_LAUNCH;
+  LoraDownArgs l;
+  a.lr = nullptr;
   if (lr_rank > 0) {
-    LoraDownArgs l;
     l.x = static_cast<const uint16_t*>(x);
     l.rows = rows;
     l.cols = cols;
@@ -156,8 +155,9 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
     l.rank = lr_rank;
     l.u = lr_u;
     l.ld_u = ld_u;
-    e = launch_lora_down(l, as_stream(stream));
+    a.lr = &l;
   }
+  hipError_t e = launch_quantize(a, as_stream(stream));
   return from_hip(e);
 }
 

@@ -6,6 +6,16 @@
 
 namespace mxq {
 
+struct LoraDownArgs {
+  const uint16_t* x;   // bf16 [rows][ldx]
+  int64_t rows, cols, ldx;
+  const uint16_t* l1t; // bf16 [rank][cols]
+  int rank;
+  float* u;            // [rows][ld_u]
+  int64_t ld_u;
+};
+hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s);
+
 struct QuantizeArgs {
   const void* x;
   int dtype;
@@ -19,21 +29,14 @@ struct QuantizeArgs {
   float* tensor_scale_out;          // NVFP4
   const float* static_tensor_scale; // NVFP4, may be null
   float* partials;                  // NVFP4 dynamic: workspace
+  const LoraDownArgs* lr;           // optional low-rank down projection (bf16 x)
 };
 
 constexpr int kAmaxPartials = 1024;  // NVFP4 phase-1 grid (workspace floats)
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s);
 
-struct LoraDownArgs {
-  const uint16_t* x;   // bf16 [rows][ldx]
-  int64_t rows, cols, ldx;
-  const uint16_t* l1t; // bf16 [rank][cols]
-  int rank;
-  float* u;            // [rows][ld_u]
-  int64_t ld_u;
-};
-hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s);
+
 
 struct GemmArgs {
   int a_fmt, w_fmt;

@@ -109,16 +109,126 @@ __device__ __forceinline__ void hadamard(float v[8], int lane) {
 }
 
 __device__ __forceinline__ float reduce_partials(const QParams& p) {
-  __shared__ float red[kThreads / 64];
+  // any workgroup of up to 1024 threads (whole waves)
+  __shared__ float red[16];
+  const int nw = (int)(blockDim.x >> 6);
   float m = 0.f;
-  for (int i = threadIdx.x; i < p.n_partials; i += kThreads) m = fmaxf(m, p.partials[i]);
+  for (int i = threadIdx.x; i < p.n_partials; i += blockDim.x) m = fmaxf(m, p.partials[i]);
   m = group_max<64>(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   m = red[0];
-#pragma unroll
-  for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red[w]);
+  for (int w = 1; w < nw; ++w) m = fmaxf(m, red[w]);
   return m;
+}
+
+// Scale and element codes of one lane's 8 consecutive values of a block
+// whose max |value| is amax (NVFP4: g is the tensor scale).  MX scales come
+// from the exponent bits and the codes from the hardware scaled converts
+// (exact RNE with saturation for a normal power-of-two scale) or threshold
+// comparisons; NVFP4 / INT4 scales are correctly rounded float64 quotients.
+template <int FMT>
+__device__ __forceinline__ void encode8(const float v[8], float amax, float g, uint32_t code[8],
+                                        uint32_t& sbyte, float& sfloat) {
+  sbyte = 0;
+  sfloat = 0.f;
+  if constexpr (FMT == FMT_MXFP4) {
+    const int e = mx_exponent(amax, 2);
+    if (e >= -126) {
+      // hardware RNE convert of x / 2**e, saturating at 6 (exact: the
+      // scale is a normal power of two)
+      const float sc = ldexpf(1.0f, e);
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const uint32_t b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[i], v[i + 1], sc, 0);
+        code[i] = b & 0xFu;
+        code[i + 1] = (b >> 4) & 0xFu;
+      }
+    } else {
+      float th[7];
+      e2m1_thresholds_pow2(e, th);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) code[i] = e2m1_encode(v[i], th);
+    }
+    sbyte = (uint32_t)(e + 127);
+  } else if constexpr (FMT == FMT_MXFP8) {
+    const int e = mx_exponent(amax, 8);
+    if (e >= -126) {
+      // hardware RNE convert of x / 2**e; it does not saturate above 464,
+      // so clamp to +-448 * 2**e first (every value there rounds to 448)
+      const float sc = ldexpf(1.0f, e), lim = 448.0f * sc;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        const float x0 = fminf(fmaxf(v[i], -lim), lim);
+        const float x1 = fminf(fmaxf(v[i + 1], -lim), lim);
+        typedef short v2s __attribute__((ext_vector_type(2)));
+        const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x0, x1, sc, false);
+        const uint32_t b = __builtin_bit_cast(uint32_t, r);
+        code[i] = b & 0xFFu;
+        code[i + 1] = (b >> 8) & 0xFFu;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) code[i] = e4m3_encode(ldexpf(v[i], -e));
+    }
+    sbyte = (uint32_t)(e + 127);
+  } else if constexpr (FMT == FMT_NVFP4) {
+    // s = RN_E4M3(amax / (6 g)) from the correctly rounded float64 quotient
+    sbyte = (g == 0.f) ? 0u : e4m3_encode_f64((double)amax / (6.0 * (double)g));
+    const double d = (double)e4m3_value(sbyte) * (double)g;   // exact
+    float th[7];
+    e2m1_thresholds_f64(d, th);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = e2m1_encode(v[i], th);
+  } else {  // INT4: s = RN_fp32(amax / 7), q = clamp(RNE(x / s), -7, 7)
+    sfloat = (float)((double)amax / 7.0);
+    const double sd = (double)sfloat;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      double q = (sfloat == 0.f) ? 0.0 : rint((double)v[i] / sd);
+      q = fmin(7.0, fmax(-7.0, q));
+      code[i] = (uint32_t)((int)q) & 0xFu;
+    }
+  }
+}
+
+// Store one lane's 8 codes (and, from the block's first lane, its scale).
+template <int FMT>
+__device__ __forceinline__ void store8(const QParams& p, uint32_t row, uint32_t col,
+                                       const uint32_t code[8], uint32_t sbyte, float sfloat,
+                                       bool scale_lane) {
+  if constexpr (FMT == FMT_MXFP8) {
+    uint2 w;
+    w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    *reinterpret_cast<uint2*>(p.codes + (int64_t)row * p.ld_codes + col) = w;
+  } else {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= code[i] << (4 * i);
+    *reinterpret_cast<uint32_t*>(p.codes + (int64_t)row * p.ld_codes + col / 2) = w;
+  }
+  if (scale_lane) {
+    if constexpr (FMT == FMT_INT4) {
+      *reinterpret_cast<float*>(p.scales + (int64_t)row * p.ld_scales + (col / 32) * 4) = sfloat;
+    } else {
+      const uint32_t blk = (FMT == FMT_NVFP4) ? col / 16 : col / 32;
+      p.scales[(int64_t)row * p.ld_scales + blk] = (uint8_t)sbyte;
+    }
+  }
+}
+
+// NVFP4 tensor scale for this call (static, or g = RN_fp32(A / 2688) from the
+// phase-1 partial maxima: the float64 quotient of two float32 values rounds
+// correctly to float32, 53 >= 2*24 + 2); workgroup 0 publishes it.
+template <int FMT>
+__device__ __forceinline__ float tensor_scale(const QParams& p) {
+  float g = 0.f;
+  if constexpr (FMT == FMT_NVFP4) {
+    g = p.g_static ? *p.g_static : (float)((double)reduce_partials(p) / 2688.0);
+    if (blockIdx.x == 0 && threadIdx.x == 0 && p.g_out) *p.g_out = g;
+  }
+  return g;
 }
 
 template <int DT, int FMT, int HAD>
@@ -126,17 +236,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QParams p) {
   constexpr int LPB = (FMT == FMT_NVFP4) ? 2 : 4;  // lanes per quantization block
   const int lane = threadIdx.x & 63;
 
-  float g = 0.f;
-  if constexpr (FMT == FMT_NVFP4) {
-    if (p.g_static) {
-      g = *p.g_static;
-    } else {
-      // tensor scale g = RN_fp32(A / 2688): the float64 quotient of two float32
-      // values rounds correctly to float32 (53 >= 2*24 + 2)
-      g = (float)((double)reduce_partials(p) / 2688.0);
-    }
-    if (blockIdx.x == 0 && threadIdx.x == 0 && p.g_out) *p.g_out = g;
-  }
+  const float g = tensor_scale<FMT>(p);
 
   const uint32_t wave_global = (blockIdx.x * kThreads + threadIdx.x) >> 6;
   const uint32_t n_waves = (gridDim.x * kThreads) >> 6;
@@ -161,93 +261,162 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QParams p) {
       for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
       const float amax = group_max<LPB>(m);
 
-      uint32_t code[8];
-      uint32_t sbyte = 0;
-      float sfloat = 0.f;
-      if constexpr (FMT == FMT_MXFP4) {
-        const int e = mx_exponent(amax, 2);
-        if (e >= -126) {
-          // hardware RNE convert of x / 2**e, saturating at 6 (exact: the
-          // scale is a normal power of two)
-          const float sc = ldexpf(1.0f, e);
+      uint32_t code[8], sbyte;
+      float sfloat;
+      encode8<FMT>(v[u], amax, g, code, sbyte, sfloat);
+      if (act[u]) store8<FMT>(p, rowv[u], colv[u], code, sbyte, sfloat, (lane & (LPB - 1)) == 0);
+    }
+  }
+}
+
+// Quantize fused with the low-rank down projection u = x L1 of the SVDQuant
+// branch (Nunchaku article, "main explanation": the 16-bit low-rank part
+// reads the same unrotated activations).  One workgroup owns 16 rows; its
+// eight waves take every eighth 128-column group.  Lane (r, q) = (lane % 16,
+// lane / 16) loads the 64 contiguous bytes of row r, columns 32q + [0, 32)
+// of the group -- exactly one 32-block (two NVFP4 16-blocks), so the block
+// amax needs no lane exchange and its codes leave as one 16-byte (FP4) or
+// 32-byte (FP8) store -- and the same registers are the four K-steps of
+// 16x16x32 bf16 MFMAs against L1^T: step j pairs x columns 32q + 8j + [0, 8)
+// with the same columns of L1^T, a consistent reordering of the sum.  The
+// waves' partial u tiles are summed in LDS.  bf16 input, no rotation,
+// columns a multiple of 128.
+constexpr int kLrRows = 16;
+constexpr int kLrWaves = 8;
+
+template <int FMT, int NT>
+__global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, LoraDownArgs lr) {
+  constexpr int U = NT <= 2 ? 2 : 1;   // groups in flight per wave
+  __shared__ float part[kLrWaves][kLrRows][16 * NT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float g = tensor_scale<FMT>(p);
+  const int64_t m0 = (int64_t)blockIdx.x * kLrRows;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const bool row_ok = m0 + r16 < lr.rows;
+  const int64_t row = row_ok ? m0 + r16 : lr.rows - 1;
+  const uint16_t* xr = lr.x + row * lr.ldx + kq * 32;
+  const uint16_t* lp = lr.l1t + (int64_t)r16 * lr.cols + kq * 32;
+  const int groups = (int)(lr.cols / 128);
+  v4f acc[NT];
 #pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            const uint32_t b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[u][i], v[u][i + 1], sc, 0);
-            code[i] = b & 0xFu;
-            code[i + 1] = (b >> 4) & 0xFu;
-          }
-        } else {
-          float th[7];
-          e2m1_thresholds_pow2(e, th);
+  for (int t = 0; t < NT; ++t) acc[t] = v4f{};
+  for (int g0 = wave; g0 < groups; g0 += kLrWaves * U) {
+    uint4 xv[U][4], lv[U][NT][4];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) code[i] = e2m1_encode(v[u][i], th);
-        }
-        sbyte = (uint32_t)(e + 127);
-      } else if constexpr (FMT == FMT_MXFP8) {
-        const int e = mx_exponent(amax, 8);
-        if (e >= -126) {
-          // hardware RNE convert of x / 2**e; it does not saturate above 464,
-          // so clamp to +-448 * 2**e first (every value there rounds to 448)
-          const float sc = ldexpf(1.0f, e), lim = 448.0f * sc;
+    for (int u = 0; u < U; ++u) {
+      const int gi = g0 + kLrWaves * u;
+      const bool ok = gi < groups;
 #pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            const float x0 = fminf(fmaxf(v[u][i], -lim), lim);
-            const float x1 = fminf(fmaxf(v[u][i + 1], -lim), lim);
-            typedef short v2s __attribute__((ext_vector_type(2)));
-            const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, x0, x1, sc, false);
-            const uint32_t b = __builtin_bit_cast(uint32_t, r);
-            code[i] = b & 0xFFu;
-            code[i + 1] = (b >> 8) & 0xFFu;
-          }
-        } else {
+      for (int j = 0; j < 4; ++j) {
+        xv[u][j] = ok ? *reinterpret_cast<const uint4*>(xr + gi * 128 + 8 * j) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) code[i] = e4m3_encode(ldexpf(v[u][i], -e));
-        }
-        sbyte = (uint32_t)(e + 127);
-      } else if constexpr (FMT == FMT_NVFP4) {
-        // s = RN_E4M3(amax / (6 g)) from the correctly rounded float64 quotient
-        sbyte = (g == 0.f) ? 0u : e4m3_encode_f64((double)amax / (6.0 * (double)g));
-        const double d = (double)e4m3_value(sbyte) * (double)g;   // exact
-        float th[7];
-        e2m1_thresholds_f64(d, th);
+        for (int t = 0; t < NT; ++t)
+          lv[u][t][j] = ok ? *reinterpret_cast<const uint4*>(lp + (int64_t)t * 16 * lr.cols + gi * 128 + 8 * j)
+                           : make_uint4(0, 0, 0, 0);
+      }
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) code[i] = e2m1_encode(v[u][i], th);
-      } else {  // INT4: s = RN_fp32(amax / 7), q = clamp(RNE(x / s), -7, 7)
-        sfloat = (float)((double)amax / 7.0);
-        const double sd = (double)sfloat;
+    for (int u = 0; u < U; ++u) {
+      const int gi = g0 + kLrWaves * u;
+      if (gi >= groups) break;
+      float v[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          double q = (sfloat == 0.f) ? 0.0 : rint((double)v[u][i] / sd);
-          q = fmin(7.0, fmax(-7.0, q));
-          code[i] = (uint32_t)((int)q) & 0xFu;
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w[4] = {xv[u][j].x, xv[u][j].y, xv[u][j].z, xv[u][j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[j][2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+          v[j][2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
         }
       }
-
-      if (act[u]) {
-        const uint32_t row = rowv[u], col = colv[u];
-        if constexpr (FMT == FMT_MXFP8) {
-          uint2 w;
-          w.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-          w.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
-          *reinterpret_cast<uint2*>(p.codes + (int64_t)row * p.ld_codes + col) = w;
-        } else {
-          uint32_t w = 0;
+      float m[4];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) w |= code[i] << (4 * i);
-          *reinterpret_cast<uint32_t*>(p.codes + (int64_t)row * p.ld_codes + col / 2) = w;
-        }
-        if ((lane & (LPB - 1)) == 0) {
-          if constexpr (FMT == FMT_INT4) {
-            *reinterpret_cast<float*>(p.scales + (int64_t)row * p.ld_scales + (col / 32) * 4) =
-                sfloat;
-          } else {
-            const uint32_t blk = (FMT == FMT_NVFP4) ? col / 16 : col / 32;
-            p.scales[(int64_t)row * p.ld_scales + blk] = (uint8_t)sbyte;
+      for (int j = 0; j < 4; ++j) {
+        m[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[j] = fmaxf(m[j], fabsf(v[j][i]));
+      }
+      float amax[4];
+      if constexpr (FMT == FMT_NVFP4) {
+        amax[0] = amax[1] = fmaxf(m[0], m[1]);
+        amax[2] = amax[3] = fmaxf(m[2], m[3]);
+      } else {
+        amax[0] = amax[1] = amax[2] = amax[3] = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+      }
+      uint32_t code[4][8], sbyte[4];
+      float sfloat[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) encode8<FMT>(v[j], amax[j], g, code[j], sbyte[j], sfloat[j]);
+      if (row_ok) {
+        const int64_t col = (int64_t)gi * 128 + kq * 32;
+        uint8_t* crow = p.codes + row * p.ld_codes;
+        if constexpr (FMT == FMT_MXFP8) {
+          uint32_t w[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            w[2 * j] = code[j][0] | (code[j][1] << 8) | (code[j][2] << 16) | (code[j][3] << 24);
+            w[2 * j + 1] = code[j][4] | (code[j][5] << 8) | (code[j][6] << 16) | (code[j][7] << 24);
           }
+          *reinterpret_cast<uint4*>(crow + col) = make_uint4(w[0], w[1], w[2], w[3]);
+          *reinterpret_cast<uint4*>(crow + col + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+        } else {
+          uint32_t w[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            w[j] = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w[j] |= code[j][i] << (4 * i);
+          }
+          *reinterpret_cast<uint4*>(crow + col / 2) = make_uint4(w[0], w[1], w[2], w[3]);
         }
+        uint8_t* srow = p.scales + row * p.ld_scales;
+        if constexpr (FMT == FMT_INT4) {
+          *reinterpret_cast<float*>(srow + (col / 32) * 4) = sfloat[0];
+        } else if constexpr (FMT == FMT_NVFP4) {
+          *reinterpret_cast<uint16_t*>(srow + col / 16) = (uint16_t)(sbyte[0] | (sbyte[2] << 8));
+        } else {
+          srow[col / 32] = (uint8_t)sbyte[0];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v8bf af = __builtin_bit_cast(v8bf, xv[u][j]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(v8bf, lv[u][t][j]),
+                                                           acc[t], 0, 0, 0);
       }
     }
   }
+  // 16x16 C layout: lane holds column lane % 16, rows 4 * (lane / 16) + q
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) part[wave][4 * kq + q][t * 16 + r16] = acc[t][q];
+  __syncthreads();
+  for (int idx = tid; idx < kLrRows * 16 * NT; idx += 64 * kLrWaves) {
+    const int r = idx / (16 * NT), c = idx % (16 * NT);
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < kLrWaves; ++w) sum += part[w][r][c];
+    if (m0 + r < lr.rows) lr.u[(m0 + r) * lr.ld_u + c] = sum;
+  }
+}
+
+template <int FMT>
+hipError_t launch_lr(int nt, dim3 grid, const QParams& p, const LoraDownArgs& lr, hipStream_t s) {
+  switch (nt) {
+    case 1: quantize_lr_kernel<FMT, 1><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 2: quantize_lr_kernel<FMT, 2><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 3: quantize_lr_kernel<FMT, 3><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 4: quantize_lr_kernel<FMT, 4><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 5: quantize_lr_kernel<FMT, 5><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 6: quantize_lr_kernel<FMT, 6><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 7: quantize_lr_kernel<FMT, 7><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 8: quantize_lr_kernel<FMT, 8><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // NVFP4 phase 1: per-workgroup max |r| over the (rotated) tensor.
@@ -477,6 +646,26 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
                        ? dispatch_amax<DT_BF16>(a.hadamard_n, dim3(pb), p, a.partials, s)
                        : dispatch_amax<DT_F32>(a.hadamard_n, dim3(pb), p, a.partials, s);
     if (e != hipSuccess) return e;
+  }
+  if (a.lr && a.lr->rank > 0) {
+    if (a.dtype == DT_BF16 && a.hadamard_n == 0 && a.lr->rank <= 128 && a.cols % 128 == 0) {
+      const dim3 g((unsigned)((a.rows + kLrRows - 1) / kLrRows));
+      const int nt = a.lr->rank / 16;
+      switch (a.fmt) {
+        case FMT_MXFP4: return launch_lr<FMT_MXFP4>(nt, g, p, *a.lr, s);
+        case FMT_MXFP8: return launch_lr<FMT_MXFP8>(nt, g, p, *a.lr, s);
+        case FMT_NVFP4: return launch_lr<FMT_NVFP4>(nt, g, p, *a.lr, s);
+        case FMT_INT4: return launch_lr<FMT_INT4>(nt, g, p, *a.lr, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+    // rotated activations (or columns not a multiple of 128): quantize, then
+    // u from the unrotated x in its own pass
+    hipError_t e = (a.dtype == DT_BF16)
+                       ? dispatch_fmt<DT_BF16>(a.fmt, a.hadamard_n, dim3(blocks), p, s)
+                       : dispatch_fmt<DT_F32>(a.fmt, a.hadamard_n, dim3(blocks), p, s);
+    if (e != hipSuccess) return e;
+    return launch_lora_down(*a.lr, s);
   }
   return (a.dtype == DT_BF16)
              ? dispatch_fmt<DT_BF16>(a.fmt, a.hadamard_n, dim3(blocks), p, s)

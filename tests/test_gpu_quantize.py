@@ -96,20 +96,35 @@ def test_edge_shapes():
         mxq.quantize(gu.to_dev_f32(np.zeros((2, 96), np.float32)), mxq.MXFP4, hadamard=64)
 
 
-def test_lowrank_down():
+@pytest.mark.parametrize("fmt,r,had,k", [("MXFP4", 32, 0, 640), ("MXFP8", 16, 0, 640),
+                                          ("NVFP4", 128, 0, 640), ("INT4", 32, 0, 640),
+                                          ("NVFP4", 48, 0, 1152), ("MXFP4", 32, 16, 640),
+                                          ("NVFP4", 16, 32, 640), ("MXFP8", 32, 0, 608)])
+def test_lowrank_down(fmt, r, had, k):
+    """Quantize with the low-rank down projection u = x L1 (fused into the
+    quantize pass without rotation and with columns a multiple of 128, else
+    a separate pass): codes and scales bit-exact, u within 1e-5 of
+    sum |x| |L1|; ragged rows (100 = 6 * 16 + 4)."""
     import torch
     import fp8_quantized_linear_mxq_amd as mxq
-    rng = np.random.default_rng(8)
-    m, k, r = 100, 640, 32
-    xb = wl.f32_to_bf16_bits((rng.standard_t(3, size=(m, k))).astype(np.float32))
+    rng = np.random.default_rng(8 + r + had + k)
+    m = 100
+    xb = wl.f32_to_bf16_bits((rng.standard_t(3, size=(m, k)) * 3).astype(np.float32))
+    xb[7, :64] = 0                                   # all-zero blocks
     l1 = wl.f32_to_bf16_bits(rng.normal(0, 0.02, size=(k, r)).astype(np.float32))
     l1t = np.ascontiguousarray(l1.T)
     u = torch.empty((m, r), dtype=torch.float32, device="cuda")
-    gu.say("quantize + fused low-rank down projection")
-    mxq.quantize(gu.to_dev_bf16(xb), mxq.MXFP4, l1t=gu.to_dev_bf16(l1t), u=u)
-    xv = wl.bf16_to_f32(xb).astype(np.float64)
+    gu.say(f"quantize {fmt} had={had} + low-rank down projection rank {r}")
+    q = mxq.quantize(gu.to_dev_bf16(xb), gu.FMT_ID[fmt], hadamard=had, l1t=gu.to_dev_bf16(l1t), u=u)
+    xv = wl.bf16_to_f32(xb)
+    want = gu.oracle_quant(xv, fmt, had=had, mant_bits=7)
+    assert np.array_equal(gu.dev_scales(q, fmt), want["scales"])
+    assert np.array_equal(gu.unpack_dev_codes(q, fmt), want["codes"])
+    if fmt == "NVFP4":
+        assert float(q.tensor_scale.cpu()[0]) == float(want["g"])
+    x64 = xv.astype(np.float64)
     lv = wl.bf16_to_f32(l1).astype(np.float64)
-    ref = xv @ lv
-    bound = np.abs(xv) @ np.abs(lv)
+    ref = x64 @ lv
+    bound = np.abs(x64) @ np.abs(lv)
     err = np.abs(u.cpu().numpy().astype(np.float64) - ref)
     assert np.all(err <= 1e-5 * bound), float(np.max(err / bound))
