@@ -11,8 +11,11 @@ Infinity Cache, so every step reads from HBM.
 
 Prints one JSON line.  ``value`` is whole-step GEMM throughput (2 M N K per
 step / step time) in TFLOP/s.  ``roofline`` describes the dominant kernel
-(the GEMM), timed per launch with HIP events on its stream; ``cpu_baseline``
-times the CPU oracle on a bounded sample of the same workload.
+(the GEMM): its launches over all buffer sets are captured in a HIP graph and
+replayed between HIP events on the replay stream, which gives the average
+launch duration without host launch gaps (the quantize kernel is timed the
+same way); ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same workload.
 """
 from __future__ import annotations
 
@@ -114,6 +117,28 @@ def set_bytes(s) -> int:
     return tot
 
 
+def graph_avg_ms(torch, calls, min_launches: int) -> float:
+    """Average duration of one call, from HIP-graph replays of all calls."""
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, -(-min_launches // len(calls)))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * len(calls))
+
+
 def cpu_baseline(w: wl.Workload, budget_s: float = 15.0) -> dict:
     """The oracle, as it stands, on a bounded row sample of the workload:
     activation quantize + float64 GEMM (+ low-rank branch) per row."""
@@ -188,18 +213,11 @@ def main() -> int:
     n_sets = max(2, int(np.ceil(512e6 / per_set)) + 1)
     sets = one + make_sets(w, n_sets - 1, mxq, torch)
     fa = wl_fmt(mxq, w.act_fmt)
-    stream = torch.cuda.current_stream()
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(s):
         mxq.quantize(s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], u=s["u"], out=s["qa"],
                      workspace=s["ws"])
-        if ev is not None:
-            ev[1].record(stream)
         mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"])
-        if ev is not None:
-            ev[2].record(stream)
 
     for i in range(args.warmup):
         step(sets[i % n_sets])
@@ -210,13 +228,14 @@ def main() -> int:
         step(sets[i % n_sets])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-kernel durations with events on the launch stream (separate pass)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(sets[i % n_sets], evs[i])
-    torch.cuda.synchronize()
-    q_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    g_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    # per-kernel durations: each kernel's launches over all buffer sets are
+    # captured in a HIP graph and replayed between two HIP events on the
+    # replay stream, so host launch gaps do not count
+    q_ms = graph_avg_ms(torch, [lambda s=s: mxq.quantize(
+        s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], u=s["u"], out=s["qa"], workspace=s["ws"])
+        for s in sets], args.steps)
+    g_ms = graph_avg_ms(torch, [lambda s=s: mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"])
+                                for s in sets], args.steps)
     if args.copy_probe:
         a = torch.empty((1 << 28,), dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)

@@ -1,0 +1,78 @@
+"""GPU: the library's launches captured in a HIP graph (as the benchmark
+times them) give, on every replay, bit-identical codes, scales, tensor
+scales, low-rank u and outputs to the eager calls.  Replays are separated by
+unrelated eager work and synchronizations."""
+import numpy as np
+import pytest
+
+from fp8_quantized_linear_mxq_amd import workloads as wl
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # (activation format, weight format, hadamard, rank)
+    ("MXFP8", "MXFP4", 0, 0),
+    ("NVFP4", "NVFP4", 16, 0),
+    ("MXFP4", "MXFP4", 0, 32),
+    ("MXFP8", "NVFP4", 0, 16),
+]
+
+
+@pytest.mark.parametrize("fa,fw,had,rank", CASES)
+def test_graph_replay_matches_eager(fa, fw, had, rank):
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    m, k, n = 300, 1024, 520
+    gu.say(f"graph replay {fa}x{fw} had={had} rank={rank}")
+    rng = np.random.default_rng(11 + rank + had)
+    x = gu.to_dev_bf16(wl.f32_to_bf16_bits((rng.standard_t(3, size=(m, k)) * 2).astype(np.float32)))
+    wf = gu.to_dev_f32(rng.normal(0, 0.02, size=(n, k)).astype(np.float32))
+    qw = mxq.quantize(wf, gu.FMT_ID[fw], hadamard=had)
+    l1t = l2t = None
+    if rank:
+        l1t = gu.to_dev_bf16(wl.f32_to_bf16_bits(rng.normal(0, 0.02, (rank, k)).astype(np.float32)))
+        l2t = gu.to_dev_bf16(wl.f32_to_bf16_bits(rng.normal(0, 0.02, (n, rank)).astype(np.float32)))
+    fmt_a = gu.FMT_ID[fa]
+    ws = torch.empty((max(16, mxq.workspace_size(1, m, k, fmt_a)),), dtype=torch.uint8, device="cuda")
+
+    def buffers():
+        q = mxq.empty_qtensor(fmt_a, m, k)
+        u = torch.empty((m, rank), dtype=torch.float32, device="cuda") if rank else None
+        y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        return q, u, y
+
+    def run(q, u, y):
+        mxq.quantize(x, fmt_a, hadamard=had, l1t=l1t, u=u, out=q, workspace=ws)
+        mxq.gemm(q, qw, u=u, l2t=l2t, out=y)
+
+    def snapshot(q, u, y):
+        out = [q.codes.clone(), q.scales.clone(), y.clone()]
+        if q.tensor_scale is not None:
+            out.append(q.tensor_scale.clone())
+        if u is not None:
+            out.append(u.clone())
+        return out
+
+    eager = buffers()
+    run(*eager)
+    torch.cuda.synchronize()
+    want = snapshot(*eager)
+
+    cap = buffers()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run(*cap)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in snapshot(*cap):
+            t.fill_(0) if t.dtype != torch.bfloat16 else t.fill_(-3.0)
+        # unrelated eager work between replays, on the same buffers' neighbours
+        run(*eager)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = snapshot(*cap)
+        for a, b in zip(got, want):
+            assert torch.equal(a, b), f"replay {rep}: a graph output differs from eager"
