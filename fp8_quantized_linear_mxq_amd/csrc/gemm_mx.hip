@@ -16,8 +16,9 @@
 // chosen by op_sel.
 //
 // Organisation:
-//  * workgroup tile (64*TM) x (64*TN), four waves in a 2 x 2 grid, each wave
-//    (32*TM) x (32*TN) = TM*TN MFMA tiles; K-tile 128 (two MFMA K-steps);
+//  * workgroup tile (32*TM*WGM) x (64*TN), waves in a WGM x 2 grid (4 or 8
+//    waves), each wave (32*TM) x (32*TN) = TM*TN MFMA tiles; K-tile 128 (two
+//    MFMA K-steps);
 //  * code and scale tiles stream into a 3-stage LDS ring with direct
 //    global->LDS loads three K-tiles ahead of the MFMAs (no register
 //    staging); each lane's load address is chosen so the bytes land in the
@@ -41,13 +42,16 @@ constexpr int RB = BK / 2;        // bytes per row per K-tile (E2M1)
 constexpr int CH = RB / 16;       // 16-byte chunks per row
 constexpr int kSlab = 16;         // K-tiles per fp32 slab when slabbing
 
-template <int TM, int TN, bool SLAB, bool LR>
-__global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
-  constexpr int TBM = 64 * TM, TBN = 64 * TN;
+template <int TM, int TN, int WGM, bool SLAB, bool LR>
+__global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) {
+  constexpr int NW = 2 * WGM;                      // waves: WGM (rows) x 2 (columns)
+  constexpr int TBM = 32 * TM * WGM, TBN = 64 * TN;
   constexpr int A_STAGE = TBM * RB, W_STAGE = TBN * RB;
-  constexpr int S_STAGE = scale_region_bytes<TBM, 4, TBN, 4>();
-  constexpr int STAGE = A_STAGE + W_STAGE + S_STAGE;
-  constexpr int NT = (TBM + TBN) * CH / 256 + S_STAGE / 1024;   // loads per wave per K-tile
+  constexpr int S_STAGE = scale_region_bytes<TBM, 4, TBN, 4, NW>();
+  constexpr bool PAD = (TBM * CH / 64) % NW != 0 || (TBN * CH / 64) % NW != 0;
+  constexpr int STAGE = A_STAGE + W_STAGE + S_STAGE + (PAD ? 1024 : 0);
+  constexpr int NT = tile_loads<TBM, RB, NW>() + tile_loads<TBN, RB, NW>() +
+                     S_STAGE / (256 * NW);   // loads per wave per K-tile
   // three separate arrays: reads of one stage are visibly independent of the
   // loads in flight into the others, so the compiler adds no wait for them
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
@@ -82,9 +86,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
   auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const bool past = kt >= KT;   // past the end of K: a tile of zeros
     kt = past ? KT - 1 : kt;
-    issue_tile<TBM, RB>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past);
-    issue_tile<TBN, RB>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past);
-    issue_scale_tile<TBM, 4, TBN, 4>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane, past);
+    uint8_t* pad = st + A_STAGE + W_STAGE + S_STAGE;
+    issue_tile<TBM, RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad);
+    issue_tile<TBN, RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad);
+    issue_scale_tile<TBM, 4, TBN, 4, NW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane, past);
   };
   struct Frag {
     v4i a[TM][2], w[TN][2];
@@ -210,22 +215,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mx_kernel(GemmP p, int gm) {
   // each wave stages its output rows in its own slice of one of them
   wait_lgkmcnt0();
   __syncthreads();
-  static_assert(2 * 32 * (TN * 64 + 16) <= STAGE, "two staging slices per stage");
-  uint8_t* region = (wave < 2 ? st0 : st1) + (wave & 1) * 32 * (TN * 64 + 16);
+  constexpr int RG = 32 * (TN * 64 + 16), SL = STAGE / RG;   // staging slices per stage
+  static_assert(3 * SL >= NW, "a staging slice per wave");
+  uint8_t* region = (wave / SL == 0 ? st0 : wave / SL == 1 ? st1 : st2) + (wave % SL) * RG;
   epilogue_tr<LR, TM, TN>(p, acc, 1.0f, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
 }
 
-template <int TM, int TN, bool SLAB>
+template <int TM, int TN, int WGM, bool SLAB>
 hipError_t launch_cfg(bool lr, GemmP p, hipStream_t s) {
-  p.tiles_m = (p.M + 64 * TM - 1) / (64 * TM);
+  p.tiles_m = (p.M + 32 * TM * WGM - 1) / (32 * TM * WGM);
   p.tiles_n = (p.N + 64 * TN - 1) / (64 * TN);
   const int tiles = p.tiles_m * p.tiles_n;
   // tile-rows per group: one XCD's share (tiles / 8) as a near-square block
   int gm = 1;
   while (gm * 2 <= p.tiles_m && gm * 2 * gm * 2 <= (tiles + 7) / 8) gm *= 2;
   const dim3 grid(tiles);
-  if (lr) gemm_mx_kernel<TM, TN, SLAB, true><<<grid, kThreads, 0, s>>>(p, gm);
-  else gemm_mx_kernel<TM, TN, SLAB, false><<<grid, kThreads, 0, s>>>(p, gm);
+  if (lr) gemm_mx_kernel<TM, TN, WGM, SLAB, true><<<grid, 128 * WGM, 0, s>>>(p, gm);
+  else gemm_mx_kernel<TM, TN, WGM, SLAB, false><<<grid, 128 * WGM, 0, s>>>(p, gm);
   return hipGetLastError();
 }
 
@@ -241,7 +247,7 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
   p.bias = a.bias;
   p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
   const bool lr = a.rank > 0;
-  if (a.K / BK > 2 * kSlab) return launch_cfg<2, 2, true>(lr, p, s);
+  if (a.K / BK > 2 * kSlab) return launch_cfg<2, 2, 2, true>(lr, p, s);
   // Large tiles move the fewest bytes per MFMA; pick the one whose tile count
   // fills the 256 compute units in the fewest rounds, per unit of tile work.
   const int64_t cu = 256;
@@ -252,9 +258,11 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
   const int64_t c43 = rounds(256, 192) * 12 * 10;   // 4x3 MFMA tiles per wave
   const int64_t c44 = rounds(256, 256) * 16 * 10;
   const int64_t c22 = rounds(128, 128) * 4 * 16;    // small tiles run ~60% as efficiently
-  if (c22 < c43 && c22 < c44) return launch_cfg<2, 2, false>(lr, p, s);
-  if (c44 < c43) return launch_cfg<4, 4, false>(lr, p, s);
-  return launch_cfg<4, 3, false>(lr, p, s);
+  if (c22 < c43 && c22 < c44) return launch_cfg<2, 2, 2, false>(lr, p, s);
+  // 256-row tiles run eight waves (4 x 2, two per SIMD): one wave's waits
+  // overlap the other's MFMAs
+  if (c44 < c43) return launch_cfg<2, 4, 4, false>(lr, p, s);
+  return launch_cfg<2, 3, 4, false>(lr, p, s);
 }
 
 }  // namespace mxq

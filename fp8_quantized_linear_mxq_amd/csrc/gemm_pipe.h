@@ -26,46 +26,54 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC
 static __device__ uint8_t g_zero16[16];
 
 // Direct loads of one operand tile (ROWS rows x RB bytes of K-tile kt) into
-// an LDS stage.  The 4 waves split the tile into 64-lane instructions; slot L
-// (16 bytes) of the stage holds row L / CH, physical chunk L % CH, which is
-// logical chunk (L % CH) ^ swz(row): each lane fetches the global chunk that
-// belongs in its slot.  Rows past the operand's end re-read its last row
-// (their results are never stored); with `zero` set every lane reads zeros.
-// Issues ROWS*CH/256 loads per wave.
-template <int ROWS, int RB>
+// an LDS stage.  The tile is ROWS*CH/64 64-lane instructions, dealt to the NW
+// waves round-robin; slot L (16 bytes) of the stage holds row L / CH, physical
+// chunk L % CH, which is logical chunk (L % CH) ^ swz(row): each lane fetches
+// the global chunk that belongs in its slot.  Rows past the operand's end
+// re-read its last row (their results are never stored); with `zero` set every
+// lane reads zeros.  Every wave issues tile_loads<ROWS, RB, NW>() loads; where
+// the count does not divide evenly the spare ones copy zeros into `pad` (1 KB),
+// so each wave's memory counter advances by the same amount.
+template <int ROWS, int RB, int NW>
+constexpr int tile_loads() { return (ROWS * RB / 1024 + NW - 1) / NW; }
+
+template <int ROWS, int RB, int NW = 4>
 __device__ __forceinline__ void issue_tile(const uint8_t* base, int64_t ld, int row0, int nrows,
                                            int kt, uint8_t* stage, int wave, int lane,
-                                           bool zero = false) {
+                                           bool zero = false, uint8_t* pad = nullptr) {
   constexpr int CH = RB / 16;
-  constexpr int PER_WAVE = ROWS * CH / 4;
-  static_assert(PER_WAVE % 64 == 0, "tile must split into whole 64-lane loads per wave");
+  constexpr int TOTAL = ROWS * CH / 64;
+  static_assert(ROWS * CH % 64 == 0, "tile must split into whole 64-lane loads");
 #pragma unroll
-  for (int t = 0; t < PER_WAVE / 64; ++t) {
-    const int slot0 = wave * PER_WAVE + t * 64;
+  for (int t = 0; t < tile_loads<ROWS, RB, NW>(); ++t) {
+    const int idx = t * NW + wave;
+    const bool real = (TOTAL % NW == 0) || idx < TOTAL;
+    const int slot0 = (real ? idx : 0) * 64;
     const int L = slot0 + lane;
     const int r = L / CH, pc = L % CH;
     int grow = row0 + r;
     grow = grow < nrows ? grow : nrows - 1;
     const uint8_t* src = base + (int64_t)grow * ld + (int64_t)kt * RB + ((pc ^ swz<CH>(r)) * 16);
-    src = zero ? g_zero16 : src;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage + slot0 * 16), 16, 0, 0);
+    src = (zero || !real) ? g_zero16 : src;
+    uint8_t* dst = real ? stage + slot0 * 16 : pad;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
   }
 }
 
 // Direct loads of one K-tile's block-scale bytes of both operands, one dword
 // per lane: TBM rows of A (SBA bytes each), then TBN rows of W (SBW bytes
 // each); lanes past the end re-read a valid dword into padding; with `zero`
-// set every lane reads zeros.  Issues ceil((TBM*SBA + TBN*SBW) / 1024) loads
-// per wave.
-template <int TBM, int SBA, int TBN, int SBW>
+// set every lane reads zeros.  Issues ceil((TBM*SBA + TBN*SBW) / (256*NW))
+// loads per wave.
+template <int TBM, int SBA, int TBN, int SBW, int NW = 4>
 __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0, int kt,
                                                  uint8_t* region, int wave, int lane,
                                                  bool zero = false) {
   constexpr int DA = TBM * SBA / 4, D = DA + TBN * SBW / 4;
-  constexpr int PERW = (D + 255) / 256;
+  constexpr int PERW = (D + 64 * NW - 1) / (64 * NW);
 #pragma unroll
   for (int t = 0; t < PERW; ++t) {
-    const int slot0 = (t * 4 + wave) * 64;
+    const int slot0 = (t * NW + wave) * 64;
     const int d = slot0 + lane;
     const uint8_t* src;
     if (d < DA) {
@@ -85,9 +93,9 @@ __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0,
   }
 }
 
-template <int TBM, int SBA, int TBN, int SBW>
+template <int TBM, int SBA, int TBN, int SBW, int NW = 4>
 constexpr int scale_region_bytes() {
-  return ((TBM * SBA / 4 + TBN * SBW / 4 + 255) / 256) * 1024;
+  return ((TBM * SBA / 4 + TBN * SBW / 4 + 64 * NW - 1) / (64 * NW)) * 256 * NW;
 }
 
 // Workgroup -> output tile.  Workgroups are dealt to the 8 XCDs round-robin;
