@@ -68,8 +68,37 @@ def quantize_bytes(w: wl.Workload) -> int:
     return rd + wr
 
 
-def make_sets(w: wl.Workload, n_sets: int, mxq, torch):
+def mixed_weights(w: wl.Workload, mxq, torch):
+    """Per-output-channel format choice on the conv weight and its groups,
+    quantized once (outside the timed region)."""
+    w0 = torch.from_numpy(wl.weights(w)).cuda()
+    _, _, perm, counts, g = mxq.select_format(w0)
+    cnt = counts.cpu().tolist()
+    groups, off = [], 0
+    for ci, fmt in enumerate((mxq.INT4, mxq.MXFP4, mxq.NVFP4)):
+        rows = perm[off:off + cnt[ci]].long()
+        groups.append(mxq.quantize(w0.index_select(0, rows).contiguous(), fmt,
+                                   static_tensor_scale=g if fmt == mxq.NVFP4 else None)
+                      if cnt[ci] else mxq.empty_qtensor(fmt, 0, w.k))
+        off += cnt[ci]
+    del w0
+    return groups, perm, cnt
+
+
+def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None):
     """Device buffer sets: activations, pre-quantized weights, outputs."""
+    if w.w_fmt == "MIXED":
+        act = wl.im2col(wl.conv_latent(w))
+        x0 = torch.from_numpy(act.view(np.int16)).view(torch.bfloat16).cuda()
+        del act
+        groups, perm, _ = mixed
+        sets = []
+        for i in range(n_sets):
+            sets.append(dict(x=x0 if i == 0 else x0.clone(), groups=groups, perm=perm,
+                             qa=mxq.empty_qtensor(mxq.MXFP8, w.m, w.k),
+                             out=torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")))
+        torch.cuda.synchronize()
+        return sets
     act = wl.activations(w)
     wt = wl.weights(w)
     fa, fw = wl_fmt(mxq, w.act_fmt), wl_fmt(mxq, w.w_fmt)
@@ -105,7 +134,10 @@ def wl_fmt(mxq, name: str) -> int:
 
 def set_bytes(s) -> int:
     tot = 0
+    vals = []
     for v in s.values():
+        vals.extend(v if isinstance(v, list) else [v])
+    for v in vals:
         if v is None:
             continue
         if hasattr(v, "codes"):
@@ -198,26 +230,35 @@ def main() -> int:
               "(the layer shards by output channels; see the design notes)", file=sys.stderr)
         return 2
     w = wl.WORKLOADS[args.workload]
-    if w.w_fmt == "MIXED":
-        print("the mixed-format convolution layer is a parity-test case, not a bench line",
-              file=sys.stderr)
-        return 2
 
     import torch
 
     import fp8_quantized_linear_mxq_amd as mxq
     mxq.load()
     torch.cuda.set_device(0)
-    one = make_sets(w, 1, mxq, torch)
+    mixed = mixed_weights(w, mxq, torch) if w.w_fmt == "MIXED" else None
+    one = make_sets(w, 1, mxq, torch, mixed)
     per_set = set_bytes(one[0])
     n_sets = max(2, int(np.ceil(512e6 / per_set)) + 1)
-    sets = one + make_sets(w, n_sets - 1, mxq, torch)
+    sets = one + make_sets(w, n_sets - 1, mxq, torch, mixed)
     fa = wl_fmt(mxq, w.act_fmt)
 
+    def quant(s):
+        if mixed:
+            mxq.quantize(s["x"], fa, out=s["qa"])
+        else:
+            mxq.quantize(s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], u=s["u"], out=s["qa"],
+                         workspace=s["ws"])
+
+    def gemm(s):
+        if mixed:
+            mxq.gemm_mixed(s["qa"], s["groups"], s["perm"], w.n, out=s["out"])
+        else:
+            mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"])
+
     def step(s):
-        mxq.quantize(s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], u=s["u"], out=s["qa"],
-                     workspace=s["ws"])
-        mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"])
+        quant(s)
+        gemm(s)
 
     for i in range(args.warmup):
         step(sets[i % n_sets])
@@ -231,11 +272,8 @@ def main() -> int:
     # per-kernel durations: each kernel's launches over all buffer sets are
     # captured in a HIP graph and replayed between two HIP events on the
     # replay stream, so host launch gaps do not count
-    q_ms = graph_avg_ms(torch, [lambda s=s: mxq.quantize(
-        s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], u=s["u"], out=s["qa"], workspace=s["ws"])
-        for s in sets], args.steps)
-    g_ms = graph_avg_ms(torch, [lambda s=s: mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"])
-                                for s in sets], args.steps)
+    q_ms = graph_avg_ms(torch, [lambda s=s: quant(s) for s in sets], args.steps)
+    g_ms = graph_avg_ms(torch, [lambda s=s: gemm(s) for s in sets], args.steps)
     if args.copy_probe:
         a = torch.empty((1 << 28,), dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -283,7 +321,10 @@ def main() -> int:
                      "frac_hbm": round(qbytes / (q_ms * 1e-3) / 1e9 / HBM_GBPS, 4)},
         "kernel_source_digest": kernel_source_digest(),
     }
-    if not args.no_cpu_baseline:
+    if mixed:
+        rec["config"]["weight_groups"] = {"INT4": mixed[2][0], "MXFP4": mixed[2][1],
+                                          "NVFP4": mixed[2][2]}
+    if not args.no_cpu_baseline and not mixed:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
     return 0
