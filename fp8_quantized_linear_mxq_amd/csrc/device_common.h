@@ -116,6 +116,35 @@ __device__ __forceinline__ void e2m1_thresholds_f64(double d, float u[7]) {
   }
 }
 
+// The same thresholds for d = s * g (s an E4M3 value, g a positive fp32)
+// without float64 products.  d = d_hi + d_lo exactly (fma residual; s has 4
+// significant bits, so d_lo is short); t = mid * d = t_hi + e with t_hi the
+// rounded mid * d_hi and e = (fma residual of mid * d_hi) + mid * d_lo, both
+// terms short and close in scale, so e is exact.  u = RN(t_hi + e) is the
+// float32 nearest t and r = e - (u - t_hi) the exact remainder t - u
+// (Fast2Sum, |t_hi| >= |e|), |r| <= half an ulp of u: the smallest float32
+// >= t (odd i) is u unless r > 0, the smallest > t (even i) u unless r >= 0.
+// Valid while every residual is a normal float32; smaller d (below 2**-60)
+// takes the float64 path.
+__device__ __forceinline__ void e2m1_thresholds_sg(float s, float g, float u[7]) {
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  const float d_hi = s * g;
+  if (!(d_hi >= 0x1p-60f)) {          // zero, or close enough to underflow
+    e2m1_thresholds_f64((double)s * (double)g, u);
+    return;
+  }
+  const float d_lo = __builtin_fmaf(s, g, -d_hi);
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    const float t_hi = mids[i] * d_hi;
+    const float e = __builtin_fmaf(mids[i], d_hi, -t_hi) + mids[i] * d_lo;
+    const float n = t_hi + e;
+    const float r = e - (n - t_hi);
+    const bool up = (i & 1) ? (r > 0.f) : (r >= 0.f);
+    u[i] = up ? next_up_pos(n) : n;
+  }
+}
+
 // E4M3 (OCP FN: bias 7, max 448, no Inf) of an exactly scaled value v with
 // |v| < 512, nearest-even, saturating at 448.
 __device__ __forceinline__ uint32_t e4m3_encode(float v) {

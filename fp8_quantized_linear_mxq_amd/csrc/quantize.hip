@@ -7,13 +7,12 @@
 // scales, NVFP4 small groups with block and tensor scales); rotation: same
 // page, modification 3 (block-diagonal Hadamard rotation of activations).
 //
-// Work layout: the [rows, cols] input is walked as a flat sequence of 8-element
-// chunks (cols is a multiple of 32, so chunks never straddle rows and every
-// 16/32-element block is 2/4 consecutive lanes).  Each lane loads one 16-byte
-// (bf16) or 32-byte (fp32) chunk, so a wave reads 1-2 KB of contiguous memory
-// and writes its packed codes contiguously.  Block amax is a 2- or 4-lane
-// DPP reduction; the Hadamard butterfly runs in float64 registers for the
-// three in-lane stages and by lane exchange for the rest.
+// Work layout: one lane per 32-element block of a row (cols is a multiple of
+// 32): a lane loads 64 contiguous bytes of bf16 (128 of fp32), so a wave reads
+// 4-8 KB of contiguous memory; the block amax (and the two NVFP4 16-block
+// maxima) are in-lane; the 16/32-point Hadamard butterflies run in float64
+// registers in-lane (128 points: two more stages across the block's 4 lanes);
+// a lane's codes leave as one 16-byte (FP4/INT4) or 32-byte (FP8) store.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -21,7 +20,6 @@ namespace mxq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 2;
 
 struct QParams {
   const void* x;
@@ -67,45 +65,6 @@ __device__ __forceinline__ void load_chunk(const QParams& p, uint32_t row, uint3
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
-}
-
-template <int L>
-__device__ __forceinline__ void cross_stage(double h[8], int lane) {
-  const bool upper = (lane & L) != 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    double o = xor_lane_d<L>(h[i]);
-    h[i] = upper ? (o - h[i]) : (h[i] + o);
-  }
-}
-
-// r = RN_fp32(RN_fp64(c_n * S)) with S = (x_block @ H_n) summed exactly in
-// float64 by the Sylvester butterfly (element distances 1, 2, 4 in-lane, then
-// 8, 16, ... across lanes).
-template <int HAD>
-__device__ __forceinline__ void hadamard(float v[8], int lane) {
-  double h[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = (double)v[i];
-#pragma unroll
-  for (int d = 1; d < 8; d <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i & d) continue;
-      double a = h[i], b = h[i + d];
-      h[i] = a + b;
-      h[i + d] = a - b;
-    }
-  }
-  if constexpr (HAD >= 16) cross_stage<1>(h, lane);
-  if constexpr (HAD >= 32) cross_stage<2>(h, lane);
-  if constexpr (HAD >= 64) cross_stage<4>(h, lane);
-  if constexpr (HAD >= 128) cross_stage<8>(h, lane);
-  constexpr double c = had_scale<HAD>();
-  // an exactly-zero sum is the real zero: + 0.0 turns -0 into +0 and leaves
-  // every nonzero value unchanged
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (float)(c * (h[i] + 0.0));
 }
 
 __device__ __forceinline__ float reduce_partials(const QParams& p) {
@@ -175,9 +134,8 @@ __device__ __forceinline__ void encode8(const float v[8], float amax, float g, u
   } else if constexpr (FMT == FMT_NVFP4) {
     // s = RN_E4M3(amax / (6 g)) from the correctly rounded float64 quotient
     sbyte = (g == 0.f) ? 0u : e4m3_encode_f64((double)amax / (6.0 * (double)g));
-    const double d = (double)e4m3_value(sbyte) * (double)g;   // exact
     float th[7];
-    e2m1_thresholds_f64(d, th);
+    e2m1_thresholds_sg(e4m3_value(sbyte), g, th);
 #pragma unroll
     for (int i = 0; i < 8; ++i) code[i] = e2m1_encode(v[i], th);
   } else {  // INT4: s = RN_fp32(amax / 7), q = clamp(RNE(x / s), -7, 7)
@@ -231,41 +189,205 @@ __device__ __forceinline__ float tensor_scale(const QParams& p) {
   return g;
 }
 
+// Store one lane's whole 32-block: 32 codes (16 bytes FP4 / INT4, 32 bytes
+// FP8) and its scales (one E8M0 byte, two E4M3 bytes for the NVFP4 16-blocks,
+// or one fp32 INT4 scale).
+template <int FMT>
+__device__ __forceinline__ void store32(const QParams& p, int64_t row, int64_t col,
+                                        const uint32_t (&code)[4][8], const uint32_t (&sbyte)[4],
+                                        const float (&sfloat)[4]) {
+  uint8_t* crow = p.codes + row * p.ld_codes;
+  if constexpr (FMT == FMT_MXFP8) {
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[2 * j] = code[j][0] | (code[j][1] << 8) | (code[j][2] << 16) | (code[j][3] << 24);
+      w[2 * j + 1] = code[j][4] | (code[j][5] << 8) | (code[j][6] << 16) | (code[j][7] << 24);
+    }
+    *reinterpret_cast<uint4*>(crow + col) = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(crow + col + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      w[j] = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[j] |= code[j][i] << (4 * i);
+    }
+    *reinterpret_cast<uint4*>(crow + col / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  uint8_t* srow = p.scales + row * p.ld_scales;
+  if constexpr (FMT == FMT_INT4) {
+    *reinterpret_cast<float*>(srow + (col / 32) * 4) = sfloat[0];
+  } else if constexpr (FMT == FMT_NVFP4) {
+    *reinterpret_cast<uint16_t*>(srow + col / 16) = (uint16_t)(sbyte[0] | (sbyte[2] << 8));
+  } else {
+    srow[col / 32] = (uint8_t)sbyte[0];
+  }
+}
+
+// Scales and codes of one lane's 32-block held as v[4][8]: one amax for MX
+// and INT4, one per 16 values for NVFP4.
+template <int FMT>
+__device__ __forceinline__ void encode32(const float (&v)[4][8], float g, uint32_t (&code)[4][8],
+                                         uint32_t (&sbyte)[4], float (&sfloat)[4]) {
+  float m[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[j] = fmaxf(m[j], fabsf(v[j][i]));
+  }
+  float amax[4];
+  if constexpr (FMT == FMT_NVFP4) {
+    amax[0] = amax[1] = fmaxf(m[0], m[1]);
+    amax[2] = amax[3] = fmaxf(m[2], m[3]);
+  } else {
+    amax[0] = amax[1] = amax[2] = amax[3] = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+  }
+  if constexpr (FMT == FMT_NVFP4) {
+    // one scale and one threshold set per 16-block (chunks 2h, 2h + 1)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t sb = (g == 0.f) ? 0u : e4m3_encode_f64((double)amax[2 * h] / (6.0 * (double)g));
+      float th[7];
+      e2m1_thresholds_sg(e4m3_value(sb), g, th);
+#pragma unroll
+      for (int j = 2 * h; j < 2 * h + 2; ++j) {
+        sbyte[j] = sb;
+        sfloat[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) code[j][i] = e2m1_encode(v[j][i], th);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) encode8<FMT>(v[j], amax[j], g, code[j], sbyte[j], sfloat[j]);
+  }
+}
+
+// A lane's 32 consecutive values of one row (64 contiguous bytes of bf16,
+// 128 of fp32).
+template <int DT>
+__device__ __forceinline__ void load32(const QParams& p, int64_t row, int64_t col, float (&v)[4][8]) {
+  if constexpr (DT == DT_BF16) {
+    const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.x) + row * p.ldx + col);
+    uint4 w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = q[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t d[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[j][2 * i] = bf16_bits_to_f32(d[i] & 0xFFFFu);
+        v[j][2 * i + 1] = bf16_bits_to_f32(d[i] >> 16);
+      }
+    }
+  } else {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p.x) + row * p.ldx + col);
+    float4 w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = q[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[j][0] = w[2 * j].x; v[j][1] = w[2 * j].y; v[j][2] = w[2 * j].z; v[j][3] = w[2 * j].w;
+      v[j][4] = w[2 * j + 1].x; v[j][5] = w[2 * j + 1].y; v[j][6] = w[2 * j + 1].z; v[j][7] = w[2 * j + 1].w;
+    }
+  }
+}
+
+// Block-diagonal Hadamard of a lane's 32 values (element index 8j + i):
+// butterfly stages at distances 1 .. min(n, 32) / 2 in registers, then for
+// n = 128 across the 4 lanes that hold the block (lane distance 1, 2 =
+// element distance 32, 64); sums exact in float64, r = RN_fp32(RN_fp64(c_n S)).
+template <int HAD>
+__device__ __forceinline__ void hadamard32(float (&v)[4][8], int lane) {
+  double h[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) h[e] = (double)v[e >> 3][e & 7];
+  constexpr int IN = HAD < 32 ? HAD : 32;
+#pragma unroll
+  for (int d = 1; d < IN; d <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      if (e & d) continue;
+      const double a = h[e], b = h[e + d];
+      h[e] = a + b;
+      h[e + d] = a - b;
+    }
+  }
+  if constexpr (HAD == 128) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bool upper = (lane & (1 << st)) != 0;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const double o = st == 0 ? xor_lane_d<1>(h[e]) : xor_lane_d<2>(h[e]);
+        h[e] = upper ? (o - h[e]) : (h[e] + o);
+      }
+    }
+  }
+  constexpr double c = had_scale<HAD>();
+  // an exactly-zero sum is the real zero: + 0.0 turns -0 into +0
+#pragma unroll
+  for (int e = 0; e < 32; ++e) v[e >> 3][e & 7] = (float)(c * (h[e] + 0.0));
+}
+
+// Quantize with one lane per 32-block (32 consecutive values of a row):
+// coalesced 64-byte (bf16) runs per lane, in-lane amax and rotation
+// (16 / 32 points; 128 points across 4 lanes), one 16/32-byte code store per
+// lane.  Grid-stride over the rows * cols / 32 blocks.
 template <int DT, int FMT, int HAD>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QParams p) {
-  constexpr int LPB = (FMT == FMT_NVFP4) ? 2 : 4;  // lanes per quantization block
-  const int lane = threadIdx.x & 63;
-
+__global__ __launch_bounds__(kThreads) void quantize32_kernel(QParams p, uint32_t bpr, uint32_t nblk) {
   const float g = tensor_scale<FMT>(p);
+  const int lane = threadIdx.x & 63;
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b - lane < nblk; b += stride) {
+    // whole waves stay in the loop (the 128-point rotation exchanges lanes);
+    // lanes past the end work on a clamped block and store nothing
+    const bool act = b < nblk;
+    const uint32_t bb = act ? b : nblk - 1;
+    const int64_t row = bb / bpr, col = (int64_t)(bb - (uint32_t)row * bpr) * 32;
+    float v[4][8];
+    load32<DT>(p, row, col, v);
+    if constexpr (HAD > 0) hadamard32<HAD>(v, lane);
+    uint32_t code[4][8], sbyte[4];
+    float sfloat[4];
+    encode32<FMT>(v, g, code, sbyte, sfloat);
+    if (act) store32<FMT>(p, row, col, code, sbyte, sfloat);
+  }
+}
 
-  const uint32_t wave_global = (blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const uint32_t n_waves = (gridDim.x * kThreads) >> 6;
-  for (uint32_t base = wave_global * 64u * kUnroll; base < p.total;
-       base += n_waves * 64u * kUnroll) {
-    float v[kUnroll][8];
-    uint32_t rowv[kUnroll], colv[kUnroll];
-    bool act[kUnroll];
+// NVFP4 phase 1 in the same layout: per-workgroup max |r|.
+template <int DT, int HAD>
+__global__ __launch_bounds__(kThreads) void amax32_kernel(QParams p, float* partials, uint32_t bpr,
+                                                          uint32_t nblk) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t stride = gridDim.x * kThreads;
+  float m = 0.f;
+  for (uint32_t b = blockIdx.x * kThreads + threadIdx.x; b - lane < nblk; b += stride) {
+    const bool act = b < nblk;
+    const uint32_t bb = act ? b : nblk - 1;
+    const int64_t row = bb / bpr, col = (int64_t)(bb - (uint32_t)row * bpr) * 32;
+    float v[4][8];
+    load32<DT>(p, row, col, v);
+    if constexpr (HAD > 0) hadamard32<HAD>(v, lane);
+    if (act) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint32_t c = base + u * 64u + lane;
-      act[u] = c < p.total;
-      rowv[u] = act[u] ? c / p.cpr : 0u;
-      colv[u] = act[u] ? (c - rowv[u] * p.cpr) * 8u : 0u;
-      load_chunk<DT>(p, rowv[u], colv[u], act[u], v[u]);
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if constexpr (HAD > 0) hadamard<HAD>(v[u], lane);
-      float m = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
-      const float amax = group_max<LPB>(m);
-
-      uint32_t code[8], sbyte;
-      float sfloat;
-      encode8<FMT>(v[u], amax, g, code, sbyte, sfloat);
-      if (act[u]) store8<FMT>(p, rowv[u], colv[u], code, sbyte, sfloat, (lane & (LPB - 1)) == 0);
-    }
+  }
+  __shared__ float red[kThreads / 64];
+  m = group_max<64>(m);
+  if (lane == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
+    partials[blockIdx.x] = r;
   }
 }
 
@@ -419,43 +541,6 @@ hipError_t launch_lr(int nt, dim3 grid, const QParams& p, const LoraDownArgs& lr
   return hipGetLastError();
 }
 
-// NVFP4 phase 1: per-workgroup max |r| over the (rotated) tensor.
-template <int DT, int HAD>
-__global__ __launch_bounds__(kThreads) void amax_kernel(QParams p, float* partials) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t wave_global = (blockIdx.x * kThreads + threadIdx.x) >> 6;
-  const uint32_t n_waves = (gridDim.x * kThreads) >> 6;
-  float m = 0.f;
-  for (uint32_t base = wave_global * 64u * kUnroll; base < p.total;
-       base += n_waves * 64u * kUnroll) {
-    float v[kUnroll][8];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      uint32_t c = base + u * 64u + lane;
-      bool act = c < p.total;
-      uint32_t row = act ? c / p.cpr : 0u;
-      uint32_t col = act ? (c - row * p.cpr) * 8u : 0u;
-      load_chunk<DT>(p, row, col, act, v[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if constexpr (HAD > 0) hadamard<HAD>(v[u], lane);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[u][i]));
-    }
-  }
-  __shared__ float red[kThreads / 64];
-  m = group_max<64>(m);
-  if (lane == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = red[0];
-    for (int w = 1; w < kThreads / 64; ++w) r = fmaxf(r, red[w]);
-    partials[blockIdx.x] = r;
-  }
-}
-
-
 // ---------------------------------------------------------------------------
 // Per-output-channel format selection (Chameleon article, "the format is
 // chosen by the value distribution": try the available formats per output
@@ -583,35 +668,38 @@ __global__ __launch_bounds__(256) void group_kernel(const uint8_t* choice, int n
 }
 
 template <int DT, int FMT>
-hipError_t dispatch_had(int had, dim3 grid, const QParams& p, hipStream_t s) {
+hipError_t dispatch_had(int had, dim3 grid, const QParams& p, uint32_t bpr, uint32_t nblk,
+                        hipStream_t s) {
   switch (had) {
-    case 0: quantize_kernel<DT, FMT, 0><<<grid, kThreads, 0, s>>>(p); break;
-    case 16: quantize_kernel<DT, FMT, 16><<<grid, kThreads, 0, s>>>(p); break;
-    case 32: quantize_kernel<DT, FMT, 32><<<grid, kThreads, 0, s>>>(p); break;
-    case 128: quantize_kernel<DT, FMT, 128><<<grid, kThreads, 0, s>>>(p); break;
+    case 0: quantize32_kernel<DT, FMT, 0><<<grid, kThreads, 0, s>>>(p, bpr, nblk); break;
+    case 16: quantize32_kernel<DT, FMT, 16><<<grid, kThreads, 0, s>>>(p, bpr, nblk); break;
+    case 32: quantize32_kernel<DT, FMT, 32><<<grid, kThreads, 0, s>>>(p, bpr, nblk); break;
+    case 128: quantize32_kernel<DT, FMT, 128><<<grid, kThreads, 0, s>>>(p, bpr, nblk); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t dispatch_fmt(int fmt, int had, dim3 grid, const QParams& p, hipStream_t s) {
+hipError_t dispatch_fmt(int fmt, int had, dim3 grid, const QParams& p, uint32_t bpr, uint32_t nblk,
+                        hipStream_t s) {
   switch (fmt) {
-    case FMT_MXFP4: return dispatch_had<DT, FMT_MXFP4>(had, grid, p, s);
-    case FMT_MXFP8: return dispatch_had<DT, FMT_MXFP8>(had, grid, p, s);
-    case FMT_NVFP4: return dispatch_had<DT, FMT_NVFP4>(had, grid, p, s);
-    case FMT_INT4: return dispatch_had<DT, FMT_INT4>(had, grid, p, s);
+    case FMT_MXFP4: return dispatch_had<DT, FMT_MXFP4>(had, grid, p, bpr, nblk, s);
+    case FMT_MXFP8: return dispatch_had<DT, FMT_MXFP8>(had, grid, p, bpr, nblk, s);
+    case FMT_NVFP4: return dispatch_had<DT, FMT_NVFP4>(had, grid, p, bpr, nblk, s);
+    case FMT_INT4: return dispatch_had<DT, FMT_INT4>(had, grid, p, bpr, nblk, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int DT>
-hipError_t dispatch_amax(int had, dim3 grid, const QParams& p, float* partials, hipStream_t s) {
+hipError_t dispatch_amax(int had, dim3 grid, const QParams& p, float* partials, uint32_t bpr,
+                         uint32_t nblk, hipStream_t s) {
   switch (had) {
-    case 0: amax_kernel<DT, 0><<<grid, kThreads, 0, s>>>(p, partials); break;
-    case 16: amax_kernel<DT, 16><<<grid, kThreads, 0, s>>>(p, partials); break;
-    case 32: amax_kernel<DT, 32><<<grid, kThreads, 0, s>>>(p, partials); break;
-    case 128: amax_kernel<DT, 128><<<grid, kThreads, 0, s>>>(p, partials); break;
+    case 0: amax32_kernel<DT, 0><<<grid, kThreads, 0, s>>>(p, partials, bpr, nblk); break;
+    case 16: amax32_kernel<DT, 16><<<grid, kThreads, 0, s>>>(p, partials, bpr, nblk); break;
+    case 32: amax32_kernel<DT, 32><<<grid, kThreads, 0, s>>>(p, partials, bpr, nblk); break;
+    case 128: amax32_kernel<DT, 128><<<grid, kThreads, 0, s>>>(p, partials, bpr, nblk); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -634,8 +722,10 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   p.partials = a.partials;
   p.n_partials = 0;
 
-  const uint32_t per_block = kThreads * kUnroll;
-  uint32_t blocks = (p.total + per_block - 1) / per_block;
+  // one lane per 32-block
+  const uint32_t bpr = (uint32_t)(a.cols / 32);
+  const uint32_t nblk = (uint32_t)(a.rows * bpr);
+  uint32_t blocks = (nblk + kThreads - 1) / kThreads;
   if (blocks > 8192u) blocks = 8192u;
   if (blocks == 0) return hipSuccess;
 
@@ -643,8 +733,8 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
     uint32_t pb = blocks < (uint32_t)kAmaxPartials ? blocks : (uint32_t)kAmaxPartials;
     p.n_partials = (int)pb;
     hipError_t e = (a.dtype == DT_BF16)
-                       ? dispatch_amax<DT_BF16>(a.hadamard_n, dim3(pb), p, a.partials, s)
-                       : dispatch_amax<DT_F32>(a.hadamard_n, dim3(pb), p, a.partials, s);
+                       ? dispatch_amax<DT_BF16>(a.hadamard_n, dim3(pb), p, a.partials, bpr, nblk, s)
+                       : dispatch_amax<DT_F32>(a.hadamard_n, dim3(pb), p, a.partials, bpr, nblk, s);
     if (e != hipSuccess) return e;
   }
   if (a.lr && a.lr->rank > 0) {
@@ -662,14 +752,14 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
     // rotated activations (or columns not a multiple of 128): quantize, then
     // u from the unrotated x in its own pass
     hipError_t e = (a.dtype == DT_BF16)
-                       ? dispatch_fmt<DT_BF16>(a.fmt, a.hadamard_n, dim3(blocks), p, s)
-                       : dispatch_fmt<DT_F32>(a.fmt, a.hadamard_n, dim3(blocks), p, s);
+                       ? dispatch_fmt<DT_BF16>(a.fmt, a.hadamard_n, dim3(blocks), p, bpr, nblk, s)
+                       : dispatch_fmt<DT_F32>(a.fmt, a.hadamard_n, dim3(blocks), p, bpr, nblk, s);
     if (e != hipSuccess) return e;
     return launch_lora_down(*a.lr, s);
   }
   return (a.dtype == DT_BF16)
-             ? dispatch_fmt<DT_BF16>(a.fmt, a.hadamard_n, dim3(blocks), p, s)
-             : dispatch_fmt<DT_F32>(a.fmt, a.hadamard_n, dim3(blocks), p, s);
+             ? dispatch_fmt<DT_BF16>(a.fmt, a.hadamard_n, dim3(blocks), p, bpr, nblk, s)
+             : dispatch_fmt<DT_F32>(a.fmt, a.hadamard_n, dim3(blocks), p, bpr, nblk, s);
 }
 
 
@@ -685,12 +775,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   p.g_static = nullptr;
   p.partials = a.partials;
   if (a.n == 0) return hipSuccess;
-  const uint32_t per_block = kThreads * kUnroll;
-  uint32_t blocks = (p.total + per_block - 1) / per_block;
+  const uint32_t bpr = (uint32_t)(a.k / 32), nblk = (uint32_t)(a.n * bpr);
+  uint32_t blocks = (nblk + kThreads - 1) / kThreads;
   if (blocks > (uint32_t)kAmaxPartials) blocks = kAmaxPartials;
   p.n_partials = (int)blocks;
-  hipError_t e = (a.dtype == DT_BF16) ? dispatch_amax<DT_BF16>(0, dim3(blocks), p, a.partials, s)
-                                      : dispatch_amax<DT_F32>(0, dim3(blocks), p, a.partials, s);
+  hipError_t e = (a.dtype == DT_BF16)
+                     ? dispatch_amax<DT_BF16>(0, dim3(blocks), p, a.partials, bpr, nblk, s)
+                     : dispatch_amax<DT_F32>(0, dim3(blocks), p, a.partials, bpr, nblk, s);
   if (e != hipSuccess) return e;
   sp.n_cand = a.n_cand;
   for (int i = 0; i < 4; ++i) sp.cand[i] = i < a.n_cand ? a.cand[i] : 0;

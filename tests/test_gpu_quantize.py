@@ -128,3 +128,20 @@ def test_lowrank_down(fmt, r, had, k):
     bound = np.abs(x64) @ np.abs(lv)
     err = np.abs(u.cpu().numpy().astype(np.float64) - ref)
     assert np.all(err <= 1e-5 * bound), float(np.max(err / bound))
+
+
+@pytest.mark.parametrize("exp2", [-30, -50, -62, -80, -110])
+def test_nvfp4_small_tensor_scales(exp2):
+    """NVFP4 on tensors scaled by 2**exp2: the element thresholds s * g *
+    midpoint take the float32 error-free path while s * g >= 2**-60 and the
+    float64 path below; both must match the oracle bit for bit."""
+    import fp8_quantized_linear_mxq_amd as mxq
+    rng = np.random.default_rng(40 - exp2)
+    x = (rng.standard_t(3, size=(24, 256)) * 2.0 ** rng.integers(-6, 6, size=(24, 1))
+         * 2.0 ** exp2).astype(np.float32)
+    gu.say(f"NVFP4 small tensor scale 2**{exp2}")
+    q = mxq.quantize(gu.to_dev_f32(x), mxq.NVFP4)
+    want = gu.oracle_quant(x, "NVFP4")
+    assert float(q.tensor_scale.cpu()[0]) == float(want["g"])
+    assert np.array_equal(gu.dev_scales(q, "NVFP4"), want["scales"])
+    assert np.array_equal(gu.unpack_dev_codes(q, "NVFP4"), want["codes"])
