@@ -17,18 +17,20 @@
 //
 // Organisation:
 //  * workgroup tile (32*TM*WGM) x (64*TN), waves in a WGM x 2 grid (4 or 8
-//    waves), each wave (32*TM) x (32*TN) = TM*TN MFMA tiles; K-tile 128 (two
-//    MFMA K-steps);
-//  * code and scale tiles stream into a 3-stage LDS ring with direct
-//    global->LDS loads three K-tiles ahead of the MFMAs (no register
-//    staging); each lane's load address is chosen so the bytes land in the
+//    waves), each wave (32*TM) x (32*TN) = TM*TN MFMA tiles; K-tile 256
+//    (four MFMA K-steps), so every row of a tile contributes one whole
+//    128-byte line per K-tile (64-byte half lines take about 1.5x as long
+//    to stream at full occupancy);
+//  * code and scale tiles stream into a 2-stage LDS ring with direct
+//    global->LDS loads one K-tile ahead of the MFMAs (no register staging);
+//    each lane's load address is chosen so the bytes land in the
 //    XOR-swizzled slot the fragment reads expect;
-//  * fragments of K-tile kt+1 are read from LDS while the MFMAs of K-tile kt
-//    run; one barrier per K-tile;
+//  * one barrier per K-tile; a K-tile's fragments are read at the start of
+//    its step and consumed in K-step order while the next K-tile streams in;
 //  * the MFMAs compute D^T = W A^T (weight fragment first), so each lane ends
 //    up holding four consecutive output columns of one row;
-//  * past 32 K-tiles (K > 4096) the fp32 chains are flushed into a second
-//    accumulator every 16 K-tiles (small tiles only, for the registers).
+//  * past 16 K-tiles (K > 4096) the fp32 chains are flushed into a second
+//    accumulator every 8 K-tiles (small tiles only, for the registers).
 #include "device_common.h"
 #include "gemm_common.h"
 #include "gemm_pipe.h"
@@ -37,26 +39,25 @@
 namespace mxq {
 namespace {
 
-constexpr int BK = 128;           // K per tile
+constexpr int BK = 256;           // K per tile
 constexpr int RB = BK / 2;        // bytes per row per K-tile (E2M1)
 constexpr int CH = RB / 16;       // 16-byte chunks per row
-constexpr int kSlab = 16;         // K-tiles per fp32 slab when slabbing
+constexpr int KS = BK / 64;       // MFMA K-steps per K-tile
+constexpr int SB = BK / 32;       // scale bytes per row per K-tile
+constexpr int kSlab = 8;          // K-tiles per fp32 slab when slabbing
 
 template <int TM, int TN, int WGM, bool SLAB, bool LR>
 __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) {
   constexpr int NW = 2 * WGM;                      // waves: WGM (rows) x 2 (columns)
   constexpr int TBM = 32 * TM * WGM, TBN = 64 * TN;
   constexpr int A_STAGE = TBM * RB, W_STAGE = TBN * RB;
-  constexpr int S_STAGE = scale_region_bytes<TBM, 4, TBN, 4, NW>();
+  constexpr int S_STAGE = scale_region_bytes<TBM, SB, TBN, SB, NW>();
   constexpr bool PAD = (TBM * CH / 64) % NW != 0 || (TBN * CH / 64) % NW != 0;
   constexpr int STAGE = A_STAGE + W_STAGE + S_STAGE + (PAD ? 1024 : 0);
-  constexpr int NT = tile_loads<TBM, RB, NW>() + tile_loads<TBN, RB, NW>() +
-                     S_STAGE / (256 * NW);   // loads per wave per K-tile
-  // three separate arrays: reads of one stage are visibly independent of the
-  // loads in flight into the others, so the compiler adds no wait for them
+  // two separate arrays: reads of one stage are visibly independent of the
+  // loads in flight into the other, so the compiler adds no wait for them
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
 
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, gm, tm, tn);
@@ -64,50 +65,36 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, half = lane >> 5;
-  const int KT = p.K / BK;
+  const int KT = (p.K + BK - 1) / BK;
+  // a K that is an odd multiple of 128 leaves the last K-tile half full
+  const int last_ch = (p.K % BK) ? (p.K % BK) / 32 : CH;
 
-  // byte offsets within a stage of this lane's fragment and scale reads
-  uint32_t a_off[TM][2], w_off[TN][2], sa_off[TM], sw_off[TN];
+  // Byte offsets within a stage of this lane's fragment and scale reads.  At
+  // K-step s the lane supplies K = 64s + 32*half + [0, 32) of its row, i.e.
+  // chunk 2s + half, stored at chunk (2s + half) ^ swz(row).  Every row the
+  // lane reads is l32 plus a multiple of 32, all with the same swizzle, so
+  // one register per K-step serves all of them (the rows differ by constant
+  // offsets).
+  const int swl = swz<CH>(l32);
+  uint32_t a_base[KS], w_base[KS];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = wm * 32 * TM + i * 32 + l32;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) a_off[i][s] = r * RB + (((2 * s + half) ^ swz<CH>(r)) * 16);
-    sa_off[i] = A_STAGE + W_STAGE + r * 4;
+  for (int s = 0; s < KS; ++s) {
+    const uint32_t c = ((2 * s + half) ^ swl) * 16;
+    a_base[s] = (wm * 32 * TM + l32) * RB + c;
+    w_base[s] = A_STAGE + (wn * 32 * TN + l32) * RB + c;
   }
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int r = wn * 32 * TN + j * 32 + l32;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) w_off[j][s] = A_STAGE + r * RB + (((2 * s + half) ^ swz<CH>(r)) * 16);
-    sw_off[j] = A_STAGE + W_STAGE + (TBM + r) * 4;
-  }
+  const uint32_t sa_base = A_STAGE + W_STAGE + (wm * 32 * TM + l32) * SB;
+  const uint32_t sw_base = A_STAGE + W_STAGE + (TBM + wn * 32 * TN + l32) * SB;
 
   auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const bool past = kt >= KT;   // past the end of K: a tile of zeros
     kt = past ? KT - 1 : kt;
+    const int lim = kt == KT - 1 ? last_ch : CH;
     uint8_t* pad = st + A_STAGE + W_STAGE + S_STAGE;
-    issue_tile<TBM, RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad);
-    issue_tile<TBN, RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad);
-    issue_scale_tile<TBM, 4, TBN, 4, NW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane, past);
-  };
-  struct Frag {
-    v4i a[TM][2], w[TN][2];
-    uint32_t sa[TM], sw[TN];
-  };
-  auto read = [&](const uint8_t* st, Frag& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) f.a[i][s] = *reinterpret_cast<const v4i*>(st + a_off[i][s]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int s = 0; s < 2; ++s) f.w[j][s] = *reinterpret_cast<const v4i*>(st + w_off[j][s]);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) f.sa[i] = *reinterpret_cast<const uint32_t*>(st + sa_off[i]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) f.sw[j] = *reinterpret_cast<const uint32_t*>(st + sw_off[j]);
+    issue_tile<TBM, RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad, lim);
+    issue_tile<TBN, RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad, lim);
+    issue_scale_tile<TBM, SB, TBN, SB, NW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane,
+                                           past, lim / 4, lim / 4);
   };
 
   v16f acc[TM][TN];
@@ -123,57 +110,76 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
       for (int j = 0; j < TN; ++j) tot[i][j] = v16f{};
   }
 
-  auto compute = [&](const Frag& f) __attribute__((always_inline)) {
-    // the lane's E8M0 bytes for K-blocks 2s + half sit at byte 2s after the shift
-    uint32_t sa[TM], sw[TN];
+  // Read the K-tile's fragments and scales from stage `st` and multiply,
+  // the fragments of K-step s+1 read while the MFMAs of K-step s run.  The
+  // scale dword d of a row holds the E8M0 of K-blocks 4d .. 4d+3; the lane's
+  // byte for K-step s (block 2s + half) sits at byte 2(s%2) of dword s/2
+  // after shifting by 8*half.
+  auto compute = [&](const uint8_t* st) __attribute__((always_inline)) {
+    uint2 sa2[TM], sw2[TN];
+    v4i fa[2][TM], fw[2][TN];
+    auto frag = [&](int s, int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) sa[i] = f.sa[i] >> (8 * half);
+      for (int j = 0; j < TN; ++j)
+        fw[b][j] = *reinterpret_cast<const v4i*>(st + w_base[s] + j * 32 * RB);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) sw[j] = f.sw[j] >> (8 * half);
+      for (int i = 0; i < TM; ++i)
+        fa[b][i] = *reinterpret_cast<const v4i*>(st + a_base[s] + i * 32 * RB);
+    };
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int i = 0; i < TM; ++i) sa2[i] = *reinterpret_cast<const uint2*>(st + sa_base + i * 32 * SB);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sw2[j] = *reinterpret_cast<const uint2*>(st + sw_base + j * 32 * SB);
+    frag(0, 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) frag(s + 1, (s + 1) & 1);
+      uint32_t sa[TM], sw[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) sa[i] = (s < 2 ? sa2[i].x : sa2[i].y) >> (8 * half);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) sw[j] = (s < 2 ? sw2[j].x : sw2[j].y) >> (8 * half);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           // E2M1 operands use the low four dwords of the 8-dword register
-          const v8i wv = __builtin_shufflevector(f.w[j][s], f.w[j][s], 0, 1, 2, 3, -1, -1, -1, -1);
-          const v8i av = __builtin_shufflevector(f.a[i][s], f.a[i][s], 0, 1, 2, 3, -1, -1, -1, -1);
-          if (s == 0)
+          const v4i& w4 = fw[s & 1][j];
+          const v4i& a4 = fa[s & 1][i];
+          const v8i wv = __builtin_shufflevector(w4, w4, 0, 1, 2, 3, -1, -1, -1, -1);
+          const v8i av = __builtin_shufflevector(a4, a4, 0, 1, 2, 3, -1, -1, -1, -1);
+          if (s % 2 == 0)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 wv, av, acc[i][j], 4, 4, 0, (int)sw[j], 0, (int)sa[i]);
           else
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 wv, av, acc[i][j], 4, 4, 2, (int)sw[j], 2, (int)sa[i]);
         }
+    }
   };
 
-  // One K-tile.  On entry `cur` holds (or is receiving) K-tile kt's
-  // fragments and K-tiles kt+1, kt+2 are in flight into their stages (tile t
-  // lives in stage t % 3).
-  //  - wait until K-tile kt+1 has landed (kt+2 may still be in flight) and
-  //    this wave's reads of kt are complete, then barrier: every wave is done
-  //    reading stage kt % 3;
-  //  - read K-tile kt+1 into `nxt`, load K-tile kt+3 into the stage just
-  //    freed, and multiply K-tile kt, the reads and loads issued in the
-  //    shadow of the MFMAs.
-  // The loop runs a whole number of 6-step groups with no branch (which keeps
-  // the accumulators in place and each step one scheduling region); K-tiles
-  // past the end are loaded as zeros and add nothing.
-  constexpr int N_MFMA = 2 * TM * TN;
-  constexpr int N_DS = 2 * (TM + TN) + TM + TN;
-  auto step = [&](int kt, const uint8_t* st_next, uint8_t* st_cur, const Frag& cur, Frag& nxt) __attribute__((always_inline)) {
-    wait_vmcnt<NT>();
-    wait_lgkmcnt0();
+  // One K-tile (tile t lives in stage t % 2): wait until K-tile kt has
+  // landed, barrier (every wave is done reading stage (kt+1) % 2, the one
+  // K-tile kt-1 lived in), load K-tile kt+1 into it, and multiply K-tile kt.
+  // The loop runs a whole number of 2-step groups with no branch (keeping the
+  // accumulators in place); K-tiles past the end are loaded as zeros.
+  constexpr int NT = tile_loads<TBM, RB, NW>() + tile_loads<TBN, RB, NW>() +
+                     S_STAGE / (256 * NW);   // loads per wave per K-tile
+  constexpr int N_MFMA = KS * TM * TN;
+  constexpr int N_DS0 = 2 * (TM + TN);            // scales and K-step 0
+  constexpr int N_DS1 = (KS - 1) * (TM + TN);     // K-steps 1 .. KS-1
+  auto step = [&](int kt, const uint8_t* st_cur, uint8_t* st_nxt) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    read(st_next, nxt);
-    issue(kt + 3, st_cur);
-    compute(cur);
-    // interleave: two LDS reads and one global->LDS load per MFMA up front
+    issue(kt + 1, st_nxt);
+    compute(st_cur);
+    // scales and K-step 0 first; then one MFMA, one fragment read (running a
+    // K-step ahead) and one of the next K-tile's loads at a time
+    __builtin_amdgcn_sched_group_barrier(0x100, N_DS0, 0);
 #pragma unroll
     for (int k = 0; k < N_MFMA; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (2 * k < N_DS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (k < N_DS1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       if (k < NT) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     if constexpr (SLAB) {
@@ -190,21 +196,11 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   };
 
   issue(0, st0);
-  issue(1, st1);
-  issue(2, st2);
-  wait_vmcnt<2 * NT>();
-  __builtin_amdgcn_s_barrier();
-  Frag f0, f1;
-  read(st0, f0);
-  for (int kt = 0; kt < KT; kt += 6) {
-    step(kt, st1, st0, f0, f1);
-    step(kt + 1, st2, st1, f1, f0);
-    step(kt + 2, st0, st2, f0, f1);
-    step(kt + 3, st1, st0, f1, f0);
-    step(kt + 4, st2, st1, f0, f1);
-    step(kt + 5, st0, st2, f1, f0);
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, st0, st1);
+    step(kt + 1, st1, st0);
   }
-  wait_vmcnt<0>();   // the spare loads issued past the end
+  wait_vmcnt<0>();   // the zero loads issued past the end
   if constexpr (SLAB) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -216,8 +212,8 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   wait_lgkmcnt0();
   __syncthreads();
   constexpr int RG = 32 * (TN * 64 + 16), SL = STAGE / RG;   // staging slices per stage
-  static_assert(3 * SL >= NW, "a staging slice per wave");
-  uint8_t* region = (wave / SL == 0 ? st0 : wave / SL == 1 ? st1 : st2) + (wave % SL) * RG;
+  static_assert(2 * SL >= NW, "a staging slice per wave");
+  uint8_t* region = (wave / SL == 0 ? st0 : st1) + (wave % SL) * RG;
   epilogue_tr<LR, TM, TN>(p, acc, 1.0f, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
 }
 
@@ -247,7 +243,7 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
   p.bias = a.bias;
   p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
   const bool lr = a.rank > 0;
-  if (a.K / BK > 2 * kSlab) return launch_cfg<2, 2, 2, true>(lr, p, s);
+  if (a.K > 4096) return launch_cfg<2, 2, 2, true>(lr, p, s);
   // Large tiles move the fewest bytes per MFMA; pick the one whose tile count
   // fills the 256 compute units in the fewest rounds, per unit of tile work.
   const int64_t cu = 256;
@@ -255,7 +251,8 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
     const int64_t t = ((a.M + tbm - 1) / tbm) * ((a.N + tbn - 1) / tbn);
     return (t + cu - 1) / cu;
   };
-  const int64_t c43 = rounds(256, 192) * 12 * 10;   // 4x3 MFMA tiles per wave
+  // (work per tile in 64x64 output blocks, x10)
+  const int64_t c43 = rounds(256, 192) * 12 * 10;
   const int64_t c44 = rounds(256, 256) * 16 * 10;
   const int64_t c22 = rounds(128, 128) * 4 * 16;    // small tiles run ~60% as efficiently
   if (c22 < c43 && c22 < c44) return launch_cfg<2, 2, 2, false>(lr, p, s);

@@ -33,14 +33,16 @@ static __device__ uint8_t g_zero16[16];
 // re-read its last row (their results are never stored); with `zero` set every
 // lane reads zeros.  Every wave issues tile_loads<ROWS, RB, NW>() loads; where
 // the count does not divide evenly the spare ones copy zeros into `pad` (1 KB),
-// so each wave's memory counter advances by the same amount.
+// so each wave's memory counter advances by the same amount.  Chunks at or
+// past logical chunk `lim` (a K-tile cut short by the end of K) read zeros.
 template <int ROWS, int RB, int NW>
 constexpr int tile_loads() { return (ROWS * RB / 1024 + NW - 1) / NW; }
 
 template <int ROWS, int RB, int NW = 4>
 __device__ __forceinline__ void issue_tile(const uint8_t* base, int64_t ld, int row0, int nrows,
                                            int kt, uint8_t* stage, int wave, int lane,
-                                           bool zero = false, uint8_t* pad = nullptr) {
+                                           bool zero = false, uint8_t* pad = nullptr,
+                                           int lim = RB / 16) {
   constexpr int CH = RB / 16;
   constexpr int TOTAL = ROWS * CH / 64;
   static_assert(ROWS * CH % 64 == 0, "tile must split into whole 64-lane loads");
@@ -53,8 +55,10 @@ __device__ __forceinline__ void issue_tile(const uint8_t* base, int64_t ld, int 
     const int r = L / CH, pc = L % CH;
     int grow = row0 + r;
     grow = grow < nrows ? grow : nrows - 1;
-    const uint8_t* src = base + (int64_t)grow * ld + (int64_t)kt * RB + ((pc ^ swz<CH>(r)) * 16);
-    src = (zero || !real) ? g_zero16 : src;
+    const int lc = pc ^ swz<CH>(r);
+    const uint8_t* src = base + (int64_t)grow * ld + (int64_t)kt * RB + lc * 16;
+    const bool cut = lim < RB / 16 && lc >= lim;
+    src = (zero || !real || cut) ? g_zero16 : src;
     uint8_t* dst = real ? stage + slot0 * 16 : pad;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
   }
@@ -63,12 +67,14 @@ __device__ __forceinline__ void issue_tile(const uint8_t* base, int64_t ld, int 
 // Direct loads of one K-tile's block-scale bytes of both operands, one dword
 // per lane: TBM rows of A (SBA bytes each), then TBN rows of W (SBW bytes
 // each); lanes past the end re-read a valid dword into padding; with `zero`
-// set every lane reads zeros.  Issues ceil((TBM*SBA + TBN*SBW) / (256*NW))
-// loads per wave.
+// set every lane reads zeros, and so do dwords at or past dword `lim_a` of
+// an A row or `lim_w` of a W row (a K-tile cut short by the end of K).  Issues
+// ceil((TBM*SBA + TBN*SBW) / (256*NW)) loads per wave.
 template <int TBM, int SBA, int TBN, int SBW, int NW = 4>
 __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0, int kt,
                                                  uint8_t* region, int wave, int lane,
-                                                 bool zero = false) {
+                                                 bool zero = false, int lim_a = SBA / 4,
+                                                 int lim_w = SBW / 4) {
   constexpr int DA = TBM * SBA / 4, D = DA + TBN * SBW / 4;
   constexpr int PERW = (D + 64 * NW - 1) / (64 * NW);
 #pragma unroll
@@ -76,19 +82,22 @@ __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0,
     const int slot0 = (t * NW + wave) * 64;
     const int d = slot0 + lane;
     const uint8_t* src;
+    bool cut = false;
     if (d < DA) {
       int r = m0 + d / (SBA / 4);
       r = r < p.M ? r : p.M - 1;
+      cut = lim_a < SBA / 4 && d % (SBA / 4) >= lim_a;
       src = p.as + (int64_t)r * p.ldas + kt * SBA + (d % (SBA / 4)) * 4;
     } else if (d < D) {
       const int e = d - DA;
       int r = n0 + e / (SBW / 4);
       r = r < p.N ? r : p.N - 1;
+      cut = lim_w < SBW / 4 && e % (SBW / 4) >= lim_w;
       src = p.ws + (int64_t)r * p.ldws + kt * SBW + (e % (SBW / 4)) * 4;
     } else {
       src = p.as + (int64_t)(m0 < p.M ? m0 : p.M - 1) * p.ldas + kt * SBA;
     }
-    src = zero ? g_zero16 : src;
+    src = (zero || cut) ? g_zero16 : src;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + slot0 * 4), 4, 0, 0);
   }
 }
