@@ -21,10 +21,14 @@
 //    (four MFMA K-steps), so every row of a tile contributes one whole
 //    128-byte line per K-tile (64-byte half lines take about 1.5x as long
 //    to stream at full occupancy);
-//  * code and scale tiles stream into a 2-stage LDS ring with direct
-//    global->LDS loads one K-tile ahead of the MFMAs (no register staging);
-//    each lane's load address is chosen so the bytes land in the
-//    XOR-swizzled slot the fragment reads expect;
+//  * code tiles stream into a 2-stage LDS ring with direct global->LDS
+//    loads one K-tile ahead of the MFMAs (no register staging); each lane's
+//    load address is chosen so the bytes land in the XOR-swizzled slot the
+//    fragment reads expect;
+//  * scales stream two K-tiles at a time (16 contiguous bytes of each row,
+//    one 16-byte piece per lane where alignment and K allow, else four
+//    dwords) into a 2-buffer ring of their own: per-K-tile 8-byte pieces
+//    from every row cost as many cache-line requests as the codes;
 //  * one barrier per K-tile; a K-tile's fragments are read at the start of
 //    its step and consumed in K-step order while the next K-tile streams in;
 //  * the MFMAs compute D^T = W A^T (weight fragment first), so each lane ends
@@ -46,18 +50,24 @@ constexpr int KS = BK / 64;       // MFMA K-steps per K-tile
 constexpr int SB = BK / 32;       // scale bytes per row per K-tile
 constexpr int kSlab = 8;          // K-tiles per fp32 slab when slabbing
 
-template <int TM, int TN, int WGM, bool SLAB, bool LR>
+template <int TM, int TN, int WGM, bool SLAB, bool LR, bool VSC>
 __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) {
   constexpr int NW = 2 * WGM;                      // waves: WGM (rows) x 2 (columns)
   constexpr int TBM = 32 * TM * WGM, TBN = 64 * TN;
   constexpr int A_STAGE = TBM * RB, W_STAGE = TBN * RB;
-  constexpr int S_STAGE = scale_region_bytes<TBM, SB, TBN, SB, NW>();
   constexpr bool PAD = (TBM * CH / 64) % NW != 0 || (TBN * CH / 64) % NW != 0;
-  constexpr int STAGE = A_STAGE + W_STAGE + S_STAGE + (PAD ? 1024 : 0);
-  // two separate arrays: reads of one stage are visibly independent of the
-  // loads in flight into the other, so the compiler adds no wait for them
+  constexpr int STAGE = A_STAGE + W_STAGE + (PAD ? 1024 : 0);
+  // scale groups: G K-tiles (one step pair), SROW bytes per row, a buffer
+  // per group in flight
+  constexpr int G = 2;
+  constexpr int SROW = G * SB, SGRP = (TBM + TBN) * SROW;
+  static_assert(((TBM + TBN) * SROW) % 1024 == 0, "whole 64-lane scale loads");
+  // two separate code stages: reads of one are visibly independent of the
+  // loads in flight into the other, so the compiler adds no wait for them;
+  // scales are read right after the step's wait, with no load outstanding
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t scl[2 * SGRP + 1024];   // + spare-load pad
 
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, gm, tm, tn);
@@ -83,18 +93,45 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
     a_base[s] = (wm * 32 * TM + l32) * RB + c;
     w_base[s] = A_STAGE + (wn * 32 * TN + l32) * RB + c;
   }
-  const uint32_t sa_base = A_STAGE + W_STAGE + (wm * 32 * TM + l32) * SB;
-  const uint32_t sw_base = A_STAGE + W_STAGE + (TBM + wn * 32 * TN + l32) * SB;
+  const uint32_t sa_base = (wm * 32 * TM + l32) * SROW;
+  const uint32_t sw_base = (TBM + wn * 32 * TN + l32) * SROW;
 
   auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const bool past = kt >= KT;   // past the end of K: a tile of zeros
     kt = past ? KT - 1 : kt;
     const int lim = kt == KT - 1 ? last_ch : CH;
-    uint8_t* pad = st + A_STAGE + W_STAGE + S_STAGE;
+    uint8_t* pad = st + A_STAGE + W_STAGE;
     issue_tile<TBM, RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad, lim);
     issue_tile<TBN, RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad, lim);
-    issue_scale_tile<TBM, SB, TBN, SB, NW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane,
-                                           past, lim / 4, lim / 4);
+  };
+  // Scale group g (K-tiles gG .. gG+G-1) into buffer g % 2: rows of A, then
+  // rows of W, SROW bytes each.  VSC (16-byte aligned scale rows, K a
+  // multiple of G K-tiles): one 16-byte piece per lane, else one dword per
+  // lane.  Pieces past the row's scales read zeros; rows past M or N re-read
+  // the last row.  Every wave issues the same number of loads, so the code
+  // has no branch; spare ones copy zeros into a pad.
+  const int srow_bytes = p.K / 32;
+  auto issue_scales = [&](int g) __attribute__((always_inline)) {
+    constexpr int PB = VSC ? 16 : 4;   // bytes per lane
+    constexpr int PER = SROW / PB, LOADS = SGRP / (64 * PB);
+    uint8_t* buf = scl + (g & 1) * SGRP;
+    const int k0 = g * SROW;   // byte offset of the group within a scale row
+#pragma unroll
+    for (int t = 0; t < (LOADS + NW - 1) / NW; ++t) {
+      const int idx = t * NW + wave;
+      const bool real = LOADS % NW == 0 || idx < LOADS;
+      const int slot = (real ? idx : 0) * 64 + lane, r = slot / PER, q = slot % PER;
+      // both candidate rows from scalar parameters, then a select (a
+      // per-lane choice between parameters would read them from memory)
+      const int ra = min(m0 + r, p.M - 1), rw = max(min(n0 + r - TBM, p.N - 1), 0);
+      const uint8_t* pa = p.as + (int64_t)ra * p.ldas;
+      const uint8_t* pw = p.ws + (int64_t)rw * p.ldws;
+      const uint8_t* src = (r < TBM ? pa : pw) + k0 + q * PB;
+      src = real && k0 + q * PB < srow_bytes ? src : g_zero16;
+      uint8_t* dst = real ? buf + idx * 64 * PB : scl + 2 * SGRP;
+      if constexpr (VSC) __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+      else __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 4, 0, 0);
+    }
   };
 
   v16f acc[TM][TN];
@@ -115,8 +152,15 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   // scale dword d of a row holds the E8M0 of K-blocks 4d .. 4d+3; the lane's
   // byte for K-step s (block 2s + half) sits at byte 2(s%2) of dword s/2
   // after shifting by 8*half.
+  uint2 sa2[TM], sw2[TN];
+  auto read_scales = [&](int kt) __attribute__((always_inline)) {
+    const uint8_t* buf = scl + ((kt / G) & 1) * SGRP + (kt % G) * SB;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) sa2[i] = *reinterpret_cast<const uint2*>(buf + sa_base + i * 32 * SROW);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) sw2[j] = *reinterpret_cast<const uint2*>(buf + sw_base + j * 32 * SROW);
+  };
   auto compute = [&](const uint8_t* st) __attribute__((always_inline)) {
-    uint2 sa2[TM], sw2[TN];
     v4i fa[2][TM], fw[2][TN];
     auto frag = [&](int s, int b) __attribute__((always_inline)) {
 #pragma unroll
@@ -126,10 +170,6 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
       for (int i = 0; i < TM; ++i)
         fa[b][i] = *reinterpret_cast<const v4i*>(st + a_base[s] + i * 32 * RB);
     };
-#pragma unroll
-    for (int i = 0; i < TM; ++i) sa2[i] = *reinterpret_cast<const uint2*>(st + sa_base + i * 32 * SB);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) sw2[j] = *reinterpret_cast<const uint2*>(st + sw_base + j * 32 * SB);
     frag(0, 0);
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
@@ -159,22 +199,28 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   };
 
   // One K-tile (tile t lives in stage t % 2): wait until K-tile kt has
-  // landed, barrier (every wave is done reading stage (kt+1) % 2, the one
-  // K-tile kt-1 lived in), load K-tile kt+1 into it, and multiply K-tile kt.
-  // The loop runs a whole number of 2-step groups with no branch (keeping the
-  // accumulators in place); K-tiles past the end are loaded as zeros.
-  constexpr int NT = tile_loads<TBM, RB, NW>() + tile_loads<TBN, RB, NW>() +
-                     S_STAGE / (256 * NW);   // loads per wave per K-tile
+  // landed and read its scales (their group landed at least one step
+  // earlier), barrier (every wave is done reading stage (kt+1) % 2, the one
+  // K-tile kt-1 lived in, and the scale buffer of the previous group), load
+  // K-tile kt+1 (and, at a group's first K-tile, the next scale group), and
+  // multiply K-tile kt.  The loop runs a whole number of 2-step groups with
+  // no branch around the MFMAs (keeping the accumulators in place); K-tiles
+  // past the end are loaded as zeros.
+  constexpr int NT = tile_loads<TBM, RB, NW>() + tile_loads<TBN, RB, NW>();   // per wave per K-tile
   constexpr int N_MFMA = KS * TM * TN;
-  constexpr int N_DS0 = 2 * (TM + TN);            // scales and K-step 0
+  constexpr int N_DS0 = TM + TN;                  // K-step 0
   constexpr int N_DS1 = (KS - 1) * (TM + TN);     // K-steps 1 .. KS-1
-  auto step = [&](int kt, const uint8_t* st_cur, uint8_t* st_nxt) __attribute__((always_inline)) {
+  auto step = [&](int kt, const uint8_t* st_cur, uint8_t* st_nxt, bool even) __attribute__((always_inline)) {
+    // nothing of the previous step sinks below the wait
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
+    read_scales(kt);
     __builtin_amdgcn_s_barrier();
     issue(kt + 1, st_nxt);
+    if (even) issue_scales(kt / G + 1);
     compute(st_cur);
-    // scales and K-step 0 first; then one MFMA, one fragment read (running a
-    // K-step ahead) and one of the next K-tile's loads at a time
+    // K-step 0 first; then one MFMA, one fragment read (running a K-step
+    // ahead) and one of the next K-tile's loads at a time
     __builtin_amdgcn_sched_group_barrier(0x100, N_DS0, 0);
 #pragma unroll
     for (int k = 0; k < N_MFMA; ++k) {
@@ -196,9 +242,12 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   };
 
   issue(0, st0);
+  issue_scales(0);
+  wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();   // scale group 0 visible to every wave
   for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, st0, st1);
-    step(kt + 1, st1, st0);
+    step(kt, st0, st1, true);
+    step(kt + 1, st1, st0, false);
   }
   wait_vmcnt<0>();   // the zero loads issued past the end
   if constexpr (SLAB) {
@@ -225,9 +274,16 @@ hipError_t launch_cfg(bool lr, GemmP p, hipStream_t s) {
   // tile-rows per group: one XCD's share (tiles / 8) as a near-square block
   int gm = 1;
   while (gm * 2 <= p.tiles_m && gm * 2 * gm * 2 <= (tiles + 7) / 8) gm *= 2;
+  // 16-byte scale pieces need 16-byte aligned scale rows in both operands
+  // and K a multiple of two K-tiles (whole 16-byte groups)
+  const bool vsc = p.ldas % 16 == 0 && p.ldws % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(p.as) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(p.ws) % 16 == 0 && p.K % (2 * BK) == 0;
   const dim3 grid(tiles);
-  if (lr) gemm_mx_kernel<TM, TN, WGM, SLAB, true><<<grid, 128 * WGM, 0, s>>>(p, gm);
-  else gemm_mx_kernel<TM, TN, WGM, SLAB, false><<<grid, 128 * WGM, 0, s>>>(p, gm);
+  if (lr && vsc) gemm_mx_kernel<TM, TN, WGM, SLAB, true, true><<<grid, 128 * WGM, 0, s>>>(p, gm);
+  else if (lr) gemm_mx_kernel<TM, TN, WGM, SLAB, true, false><<<grid, 128 * WGM, 0, s>>>(p, gm);
+  else if (vsc) gemm_mx_kernel<TM, TN, WGM, SLAB, false, true><<<grid, 128 * WGM, 0, s>>>(p, gm);
+  else gemm_mx_kernel<TM, TN, WGM, SLAB, false, false><<<grid, 128 * WGM, 0, s>>>(p, gm);
   return hipGetLastError();
 }
 
