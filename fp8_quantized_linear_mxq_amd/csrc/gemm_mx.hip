@@ -33,6 +33,8 @@
 //    its step and consumed in K-step order while the next K-tile streams in;
 //  * the MFMAs compute D^T = W A^T (weight fragment first), so each lane ends
 //    up holding four consecutive output columns of one row;
+//  * the low-rank term u L2 is accumulated before the main loop, while the
+//    first K-tile streams in (only the sum's order changes);
 //  * past 16 K-tiles (K > 4096) the fp32 chains are flushed into a second
 //    accumulator every 8 K-tiles (small tiles only, for the registers).
 #include "device_common.h"
@@ -241,8 +243,12 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
     }
   };
 
+  // The low-rank branch goes into the accumulators first, its operands (up
+  // to 32 ranks at once) loaded right behind the first K-tile, so both
+  // latencies overlap and the MFMAs run while the pipeline fills.
   issue(0, st0);
   issue_scales(0);
+  if constexpr (LR) add_lowrank<TM, TN>(p, acc, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane);
   wait_vmcnt<0>();
   __builtin_amdgcn_s_barrier();   // scale group 0 visible to every wave
   for (int kt = 0; kt < KT; kt += 2) {
@@ -263,7 +269,7 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   constexpr int RG = 32 * (TN * 64 + 16), SL = STAGE / RG;   // staging slices per stage
   static_assert(2 * SL >= NW, "a staging slice per wave");
   uint8_t* region = (wave / SL == 0 ? st0 : st1) + (wave % SL) * RG;
-  epilogue_tr<LR, TM, TN>(p, acc, 1.0f, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
+  epilogue_tr<false, TM, TN>(p, acc, 1.0f, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
 }
 
 template <int TM, int TN, int WGM, bool SLAB>

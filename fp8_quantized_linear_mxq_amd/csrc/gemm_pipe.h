@@ -126,14 +126,100 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f_t){a, b}, v2bf_t));
 }
 
-// Epilogue for the transposed accumulator layout (the MFMAs compute
-// D^T = W A^T): lane l of tile (i, j) holds output row row0 + i*32 + l%32 and
-// the values of columns col0 + j*32 + 8g + 4(l/32) + [0,4), g = 0..3, so a
-// lane stores four consecutive bf16 outputs at once.  Adds the low-rank
-// branch u L2 (u split into bf16 halves u_hi + u_lo, residual <= 2**-17 |u|,
-// two extra K = rank MFMA passes), the bias, and applies the column map.
-// `lds_region` (32 * (TN * 64 + 16) bytes private to the wave, or null)
-// enables the staged row-wise stores.
+// The low-rank branch u L2 added into the transposed accumulators (the
+// MFMAs compute D^T = W A^T: lane l of tile (i, j) holds output row
+// row0 + i*32 + l%32 and columns col0 + j*32 + 8g + 4(l/32) + [0,4)).  u is
+// split into bf16 halves u_hi + u_lo (residual <= 2**-17 |u|): two K = rank
+// passes of bf16 MFMAs per 16 ranks.  L2 is read by output column (through
+// the column map).  The loads (lr_load, up to 32 ranks held in registers)
+// and the MFMAs (lr_mma) are separate steps, so a kernel can issue other
+// loads in between; add_lowrank does both for any rank.
+template <int TI, int TN>
+struct LrFrag {
+  float4 u[2][TI][2];   // ranks 16t + 8*half + [0, 8) of the lane's rows
+  uint4 l[2][TN];       // L2 rows (bf16) of the lane's output columns
+};
+
+template <int TI, int TN>
+__device__ __forceinline__ void lr_load(const GemmP& p, LrFrag<TI, TN>& f, int t0, int nt,
+                                        int row0, int col0, int lane) {
+  const int l32 = lane & 31, half = lane >> 5;
+  // output columns first (a map lookup only when there is a map), so the L2
+  // addresses wait on nothing but these lookups
+  int col[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) col[j] = col0 + j * 32 + l32;
+  if (p.col_map) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) col[j] = col[j] < p.N ? p.col_map[col[j]] : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) col[j] = (col[j] < p.N || p.col_map) && col[j] >= 0 && col[j] < p.n_out ? col[j] : 0;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t >= nt) break;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      int row = row0 + i * 32 + l32;
+      row = row < p.M ? row : p.M - 1;
+      const float* up = p.u + (int64_t)row * p.ld_u + (t0 + t) * 16 + half * 8;
+      f.u[t][i][0] = *reinterpret_cast<const float4*>(up);
+      f.u[t][i][1] = *reinterpret_cast<const float4*>(up + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      f.l[t][j] = *reinterpret_cast<const uint4*>(p.l2t + (int64_t)col[j] * p.rank + (t0 + t) * 16 + half * 8);
+  }
+}
+
+template <int TI, int TN>
+__device__ __forceinline__ void lr_mma(const LrFrag<TI, TN>& f, int nt, v16f (&acc)[TI][TN]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (t >= nt) break;
+    v8bf ufr_h[TI], ufr_l[TI];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const float4 f0 = f.u[t][i][0], f1 = f.u[t][i][1];
+      const float v[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+      uint32_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hi[e] = f32_to_bf16_bits(v[e]);
+        lo[e] = f32_to_bf16_bits(v[e] - bf16_bits_to_f32(hi[e]));
+      }
+      ufr_h[i] = __builtin_bit_cast(v8bf, make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                                     hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)));
+      ufr_l[i] = __builtin_bit_cast(v8bf, make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                                     lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)));
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const v8bf lf = __builtin_bit_cast(v8bf, f.l[t][j]);
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, ufr_h[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, ufr_l[i], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int TI, int TN>
+__device__ __forceinline__ void add_lowrank(const GemmP& p, v16f (&acc)[TI][TN], int row0, int col0,
+                                            int lane) {
+  for (int t0 = 0; t0 < p.rank / 16; t0 += 2) {
+    LrFrag<TI, TN> f;
+    const int nt = p.rank / 16 - t0 < 2 ? p.rank / 16 - t0 : 2;
+    lr_load<TI, TN>(p, f, t0, nt, row0, col0, lane);
+    lr_mma<TI, TN>(f, nt, acc);
+  }
+}
+
+// Epilogue for the transposed accumulator layout: scales by alpha, adds the
+// low-rank branch (LR), the bias, and applies the column map.  `lds_region`
+// (32 * (TN * 64 + 16) bytes private to the wave, or null) enables the
+// staged row-wise stores.
 template <bool LR, int TI, int TN>
 __device__ __forceinline__ void epilogue_tr(const GemmP& p, v16f (&acc)[TI][TN], float alpha,
                                             int row0, int col0, int lane,
@@ -147,43 +233,7 @@ __device__ __forceinline__ void epilogue_tr(const GemmP& p, v16f (&acc)[TI][TN],
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] *= alpha;
   }
-  if constexpr (LR) {
-    for (int t = 0; t < p.rank / 16; ++t) {
-      v8bf ufr_h[TI], ufr_l[TI];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        int row = row0 + i * 32 + l32;
-        row = row < p.M ? row : p.M - 1;
-        const float* up = p.u + (int64_t)row * p.ld_u + t * 16 + half * 8;
-        const float4 f0 = *reinterpret_cast<const float4*>(up);
-        const float4 f1 = *reinterpret_cast<const float4*>(up + 4);
-        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-        uint32_t hi[8], lo[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hi[e] = f32_to_bf16_bits(f[e]);
-          lo[e] = f32_to_bf16_bits(f[e] - bf16_bits_to_f32(hi[e]));
-        }
-        ufr_h[i] = __builtin_bit_cast(v8bf, make_uint4(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                                       hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)));
-        ufr_l[i] = __builtin_bit_cast(v8bf, make_uint4(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                                       lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)));
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = col0 + j * 32 + l32;
-        int c = n < p.N ? (p.col_map ? p.col_map[n] : n) : 0;
-        c = (c >= 0 && c < p.n_out) ? c : 0;
-        const v8bf lf = __builtin_bit_cast(
-            v8bf, *reinterpret_cast<const uint4*>(p.l2t + (int64_t)c * p.rank + t * 16 + half * 8));
-#pragma unroll
-        for (int i = 0; i < TI; ++i) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, ufr_h[i], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf, ufr_l[i], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-  }
+  if constexpr (LR) add_lowrank<TI, TN>(p, acc, row0, col0, lane);
   // stores: without a column map and with a 16-byte aligned output, each
   // 32-row tile goes through the wave's LDS region (row-major) and leaves as
   // 16-byte pieces of whole rows; otherwise each lane stores its quads
