@@ -155,28 +155,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dqp_kernel(DqpParams dp) {
   const int l32 = lane & 31, half = lane >> 5;
   const int KT = p.K / BK;
 
-  // byte offsets within a stage of this lane's fragment and scale reads
-  uint32_t a_off[TM][A_DW / 4], w_off[TN][W_DW / 4], sa_off[TM], sw_off[TN];
+  // Byte offsets within a stage of this lane's fragment and scale reads.
+  // Every row the lane reads is l32 plus a multiple of 32, and the swizzle
+  // depends on the row's low bits only, so one register per 16-byte chunk
+  // serves all row tiles (they differ by constant offsets).
+  uint32_t a_base[A_DW / 4], w_base[W_DW / 4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    const int r = wm * 32 * TM + i * 32 + l32;
-#pragma unroll
-    for (int t = 0; t < A_DW / 4; ++t) {
-      const int c = half * (A_CH / 2) + t;
-      a_off[i][t] = r * A_RB + ((c ^ swz<A_CH>(r)) * 16);
-    }
-    sa_off[i] = A_STAGE + W_STAGE + r * SBA + (SBA == 8 ? 4 * half : 0);
+  for (int t = 0; t < A_DW / 4; ++t) {
+    const int c = half * (A_CH / 2) + t;
+    a_base[t] = (wm * 32 * TM + l32) * A_RB + ((c ^ swz<A_CH>(l32)) * 16);
   }
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int r = wn * 32 * TN + j * 32 + l32;
-#pragma unroll
-    for (int t = 0; t < W_DW / 4; ++t) {
-      const int c = half * (W_CH / 2) + t;
-      w_off[j][t] = A_STAGE + r * W_RB + ((c ^ swz<W_CH>(r)) * 16);
-    }
-    sw_off[j] = A_STAGE + W_STAGE + TBM * SBA + r * SBW + (SBW == 8 ? 4 * half : 0);
+  for (int t = 0; t < W_DW / 4; ++t) {
+    const int c = half * (W_CH / 2) + t;
+    w_base[t] = A_STAGE + (wn * 32 * TN + l32) * W_RB + ((c ^ swz<W_CH>(l32)) * 16);
   }
+  const uint32_t sa_base = A_STAGE + W_STAGE + (wm * 32 * TM + l32) * SBA + (SBA == 8 ? 4 * half : 0);
+  const uint32_t sw_base =
+      A_STAGE + W_STAGE + TBM * SBA + (wn * 32 * TN + l32) * SBW + (SBW == 8 ? 4 * half : 0);
 
   auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const bool past = kt >= KT;   // past the end of K: a tile of zeros
@@ -211,25 +207,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dqp_kernel(DqpParams dp) {
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int t = 0; t < W_DW / 4; ++t) {
-        const uint4 v = *reinterpret_cast<const uint4*>(st + w_off[j][t]);
+        const uint4 v = *reinterpret_cast<const uint4*>(st + w_base[t] + j * 32 * W_RB);
         wraw[j][4 * t] = v.x; wraw[j][4 * t + 1] = v.y; wraw[j][4 * t + 2] = v.z; wraw[j][4 * t + 3] = v.w;
       }
     Scales<AK, FP16> sa[TM];
     Scales<WK, FP16> sw[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      sa[i] = lane_scales<AK, FP16>(*reinterpret_cast<const uint32_t*>(st + sa_off[i]), half);
+      sa[i] = lane_scales<AK, FP16>(*reinterpret_cast<const uint32_t*>(st + sa_base + i * 32 * SBA), half);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      sw[j] = lane_scales<WK, FP16>(*reinterpret_cast<const uint32_t*>(st + sw_off[j]), half);
+      sw[j] = lane_scales<WK, FP16>(*reinterpret_cast<const uint32_t*>(st + sw_base + j * 32 * SBW), half);
     uint4 ach[2][TM];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) ach[0][i] = *reinterpret_cast<const uint4*>(st + a_off[i][0]);
+    for (int i = 0; i < TM; ++i) ach[0][i] = *reinterpret_cast<const uint4*>(st + a_base[0] + i * 32 * A_RB);
 #pragma unroll
     for (int c = 0; c < A_NC; ++c) {
       if (c + 1 < A_NC) {
 #pragma unroll
-        for (int i = 0; i < TM; ++i) ach[(c + 1) & 1][i] = *reinterpret_cast<const uint4*>(st + a_off[i][c + 1]);
+        for (int i = 0; i < TM; ++i)
+          ach[(c + 1) & 1][i] = *reinterpret_cast<const uint4*>(st + a_base[c + 1] + i * 32 * A_RB);
       }
 #pragma unroll
       for (int kk = 0; kk < A_KS; ++kk) {
