@@ -231,8 +231,9 @@ def main() -> int:
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the layer shards by output channels; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the layer would shard by output channels, each GPU holding its own "
+              "weight rows)", file=sys.stderr)
         return 2
     w = wl.WORKLOADS[args.workload]
 

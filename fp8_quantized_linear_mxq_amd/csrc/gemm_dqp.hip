@@ -12,9 +12,9 @@
 // tensor scales multiply the accumulator in the epilogue.
 //
 // Organisation (the same pipeline as the MXFP4 kernel):
-//  * workgroup tile 256 x (64*TN), four waves in a 2 x 2 grid, each wave
-//    128 x (32*TN): every dequantized fragment feeds TN (activation) or 4
-//    (weight) MFMAs;
+//  * workgroup tile (64*TM) x (64*TN), four waves in a 2 x 2 grid, each
+//    wave (32*TM) x (32*TN): every dequantized fragment feeds TN (activation)
+//    or TM (weight) MFMAs;
 //  * raw code and scale tiles (4-bit codes are a quarter, 8-bit codes half
 //    the bytes of 16-bit tiles) stream into a 3-stage LDS ring with direct
 //    global->LDS loads two K-tiles ahead of the MFMAs;
@@ -43,7 +43,7 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 enum : int { K_NV = 0, K_MX8 = 1, K_MX4 = 2 };
 
 constexpr int BK = 128;
-constexpr int kSlab = 8;   // K-tiles (8 MFMA steps each) per fp32 slab when slabbing
+constexpr int kSlab = 6;   // K-tiles (8 MFMA steps each) per fp32 slab when slabbing
 
 template <int K> constexpr int row_bytes() { return K == K_MX8 ? 128 : 64; }
 template <int K> constexpr int scale_bytes() { return K == K_NV ? 8 : 4; }
@@ -267,27 +267,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dqp_kernel(DqpParams dp) {
     __builtin_amdgcn_s_barrier();
     issue(kt + 2, st_load);
     compute(st_cur);
-    if constexpr (SLAB) {
-      if (kt < KT && (kt + 1) % kSlab == 0) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            tot[i][j] += acc[i][j];
-            acc[i][j] = v16f{};
-          }
-      }
-    }
   };
 
-  // the loop runs a whole number of 3-step groups with no branch (keeping the
-  // accumulators in place); K-tiles past the end are loaded as zeros
+  // the loop runs a whole number of 3-step groups (slabbing: 6-step groups,
+  // each flushed into the second accumulator at its end) with no branch,
+  // keeping the accumulators in place; K-tiles past the end load as zeros
   issue(0, st0);
   issue(1, st1);
-  for (int kt = 0; kt < KT; kt += 3) {
-    step(kt, st0, st2);
-    step(kt + 1, st1, st0);
-    step(kt + 2, st2, st1);
+  if constexpr (SLAB) {
+    static_assert(kSlab == 6, "one slab per loop iteration");
+    for (int kt = 0; kt < KT; kt += 6) {
+      step(kt, st0, st2);
+      step(kt + 1, st1, st0);
+      step(kt + 2, st2, st1);
+      step(kt + 3, st0, st2);
+      step(kt + 4, st1, st0);
+      step(kt + 5, st2, st1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          tot[i][j] += acc[i][j];
+          acc[i][j] = v16f{};
+        }
+    }
+  } else {
+    for (int kt = 0; kt < KT; kt += 3) {
+      step(kt, st0, st2);
+      step(kt + 1, st1, st0);
+      step(kt + 2, st2, st1);
+    }
   }
   wait_vmcnt<0>();   // the zero loads issued past the end
   if constexpr (SLAB) {
@@ -323,9 +332,9 @@ hipError_t launch_cfg(bool lr, DqpParams dp, hipStream_t s) {
 template <int AK, int WK>
 hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
   const int64_t M = dp.g.M, N = dp.g.N;
-  // past 32 K-tiles the fp32 chains are flushed into a second accumulator,
-  // which only the small tile has the registers for
-  if (dp.g.K / BK > 4 * kSlab) return launch_cfg<AK, WK, 2, 2, true>(lr, dp, s);
+  // past 32 K-tiles the fp32 chains are flushed into a second accumulator
+  // every kSlab K-tiles, which only the small tile has the registers for
+  if (dp.g.K / BK > 32) return launch_cfg<AK, WK, 2, 2, true>(lr, dp, s);
   // Short K (under 16 K-tiles): 128x128 tiles, two workgroups per compute
   // unit, so one tile's pipeline fill and output stores overlap the other's
   // MFMAs.  Longer K: the 256-row tile that fills the 256 compute units in
