@@ -128,7 +128,7 @@ __device__ __forceinline__ uint4 dq(const uint32_t* raw, int ks, const Scales<K,
 }
 
 template <int AK, int WK, int TM, int TN, bool SLAB, bool LR>
-__global__ __launch_bounds__(kThreads, 1) void gemm_dqp_kernel(DqpParams dp) {
+__global__ __launch_bounds__(kThreads, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpParams dp) {
   const GemmP& p = dp.g;
   constexpr bool FP16 = (AK == K_NV && WK == K_NV);
   constexpr int TBM = 64 * TM, TBN = 64 * TN;
