@@ -261,6 +261,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
                                                      __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
   };
 
+  // column tiles of this wave that hold any of the N columns (wave-uniform)
+  const int live_j = n0 + wn * 64 + 32 < p.N ? 2 : (n0 + wn * 64 < p.N ? 1 : 0);
   v16f acc[2][2], tot[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -292,20 +294,26 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
         bf[ks][i] = *reinterpret_cast<const uint4*>(&sB[buf][rb * RB + ((c ^ swz<CH>(rb)) * 16)]);
       }
     if constexpr (I4) {
-      // two 32-element blocks per K-tile: exact-ish block partials, then the
-      // fp32 block scale of each output column
+      // two 32-element blocks per K-tile: exact block partials, then the fp32
+      // block scale of each output column.  A wave skips its column tiles
+      // that lie wholly past N (narrow weight groups: 20 INT4 rows).
+      auto blocks = [&](int nj) __attribute__((always_inline)) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            v16f part = mfma(af[2 * b][i], bf[2 * b][j], v16f{});
-            part = mfma(af[2 * b + 1][i], bf[2 * b + 1][j], part);
-            const float s = b == 0 ? sw[j].x : sw[j].y;
+            for (int j = 0; j < 2; ++j) {
+              if (j >= nj) continue;
+              v16f part = mfma(af[2 * b][i], bf[2 * b][j], v16f{});
+              part = mfma(af[2 * b + 1][i], bf[2 * b + 1][j], part);
+              const float s = b == 0 ? sw[j].x : sw[j].y;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) acc[i][j][q] = fmaf(part[q], s, acc[i][j][q]);
-          }
+              for (int q = 0; q < 16; ++q) acc[i][j][q] = fmaf(part[q], s, acc[i][j][q]);
+            }
+      };
+      if (live_j == 2) blocks(2);
+      else if (live_j == 1) blocks(1);
     } else {
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks)
