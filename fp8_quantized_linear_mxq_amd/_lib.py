@@ -175,9 +175,24 @@ def quantize(x, fmt: int, hadamard: int = 0, static_tensor_scale=None, l1t=None,
     return out
 
 
+def _gemm_workspace(a: QTensor, ws: list, workspace):
+    """The optional GEMM workspace: a given tensor, none (workspace=False),
+    or a fresh one sized for the largest of the weight operands ``ws``."""
+    import torch
+    if workspace is False:
+        return None, 0
+    if workspace is None:
+        n = max([workspace_size(OP_GEMM, a.rows, w.rows, w.fmt) for w in ws] + [0])
+        if n <= 0:
+            return None, 0
+        workspace = torch.empty((n,), dtype=torch.uint8, device=a.codes.device)
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
 def gemm(a: QTensor, w: QTensor, n_out: int | None = None, w_out_col=None, u=None, l2t=None,
-         bias=None, out=None, stream=None):
-    """mxq_gemm; returns the bf16 [M, n_out] output tensor."""
+         bias=None, out=None, stream=None, workspace=None):
+    """mxq_gemm; returns the bf16 [M, n_out] output tensor.  ``workspace``:
+    a device tensor, None (allocated when the route can use one) or False."""
     import torch
     lib = load()
     n_out = w.rows if n_out is None else n_out
@@ -185,15 +200,16 @@ def gemm(a: QTensor, w: QTensor, n_out: int | None = None, w_out_col=None, u=Non
         out = torch.empty((a.rows, n_out), dtype=torch.bfloat16, device=a.codes.device)
     ac, wc = a.c(), w.c()
     rank = 0 if l2t is None else l2t.shape[1]
+    wsp, wsn = _gemm_workspace(a, [w], workspace)
     st = lib.mxq_gemm(C.byref(ac), C.byref(wc), _ptr(w_out_col), _ptr(u),
                       0 if u is None else u.stride(0), _ptr(l2t), rank, _ptr(bias), _ptr(out),
-                      out.stride(0), n_out, None, 0, _stream(stream))
+                      out.stride(0), n_out, wsp, wsn, _stream(stream))
     _check("mxq_gemm", st)
     return out
 
 
 def gemm_mixed(a: QTensor, groups: list, w_perm, n_out: int, u=None, l2t=None, bias=None,
-               out=None, stream=None):
+               out=None, stream=None, workspace=None):
     """mxq_gemm_mixed over weight groups (QTensor list) and their permutation."""
     import torch
     lib = load()
@@ -202,9 +218,10 @@ def gemm_mixed(a: QTensor, groups: list, w_perm, n_out: int, u=None, l2t=None, b
     ac = a.c()
     arr = (QTensorC * len(groups))(*[g.c() for g in groups])
     rank = 0 if l2t is None else l2t.shape[1]
+    wsp, wsn = _gemm_workspace(a, groups, workspace)
     st = lib.mxq_gemm_mixed(C.byref(ac), arr, len(groups), _ptr(w_perm), _ptr(u),
                             0 if u is None else u.stride(0), _ptr(l2t), rank, _ptr(bias),
-                            _ptr(out), out.stride(0), n_out, None, 0, _stream(stream))
+                            _ptr(out), out.stride(0), n_out, wsp, wsn, _stream(stream))
     _check("mxq_gemm_mixed", st)
     return out
 

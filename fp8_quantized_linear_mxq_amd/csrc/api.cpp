@@ -84,7 +84,10 @@ int64_t mxq_workspace_size(int32_t op, int64_t rows, int64_t cols, int32_t fmt) 
       if (!known_fmt(fmt)) return -1;
       return fmt == MXQ_FMT_NVFP4 ? (int64_t)kAmaxPartials * 4 : 0;
     case MXQ_OP_GEMM:
-      return 0;
+      // rows = M, cols = N (weight rows), fmt = the weight format: narrow
+      // INT4 weight groups split K into fp32 partials
+      if (!known_fmt(fmt)) return -1;
+      return fmt == MXQ_FMT_INT4 ? gemm_dq_workspace(rows, cols) : 0;
     case MXQ_OP_SELECT:
       // amax partials, the tensor scale, per-row SSE for up to 4 candidates
       return (int64_t)kAmaxPartials * 4 + 64 + rows * 4 * 8;
@@ -188,8 +191,10 @@ static mxq_status gemm_checks(const mxq_qtensor* a, const mxq_qtensor* w, const 
 static hipError_t gemm_launch(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* col_map,
                               const float* lr_u, int64_t ld_u, const void* lr_l2t,
                               int32_t lr_rank, const void* bias, void* out, int64_t ld_out,
-                              int64_t n_out, hipStream_t s) {
+                              int64_t n_out, void* workspace, size_t ws_bytes, hipStream_t s) {
   GemmArgs g;
+  g.ws = static_cast<float*>(workspace);
+  g.ws_bytes = workspace ? (int64_t)ws_bytes : 0;
   g.a_fmt = a->fmt;
   g.w_fmt = w->fmt;
   g.a_codes = static_cast<const uint8_t*>(a->codes);
@@ -226,14 +231,13 @@ mxq_status mxq_gemm(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* w
                     const float* lr_u, int64_t ld_u, const void* lr_l2t, int32_t lr_rank,
                     const void* bias, void* out, int64_t ld_out, int64_t n_out,
                     void* workspace, size_t ws_bytes, void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   mxq_status st = gemm_checks(a, w, lr_u, ld_u, lr_l2t, lr_rank, out, ld_out, n_out);
   if (st != MXQ_OK) return st;
+  if (workspace && !aligned(workspace, 16)) return MXQ_ERR_ALIGNMENT;
   if (a->rows == 0 || w->rows == 0 || n_out == 0) return MXQ_OK;
   if (!w_out_col && w->rows > n_out) return MXQ_ERR_SHAPE;
   return from_hip(gemm_launch(a, w, w_out_col, lr_u, ld_u, lr_l2t, lr_rank, bias, out, ld_out,
-                              n_out, as_stream(stream)));
+                              n_out, workspace, ws_bytes, as_stream(stream)));
 }
 
 mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int32_t n_groups,
@@ -241,9 +245,8 @@ mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int
                           const void* lr_l2t, int32_t lr_rank, const void* bias, void* out,
                           int64_t ld_out, int64_t n_out, void* workspace, size_t ws_bytes,
                           void* stream) {
-  (void)workspace;
-  (void)ws_bytes;
   if (!w_groups || n_groups <= 0 || n_groups > 8) return MXQ_ERR_INVALID_ARG;
+  if (workspace && !aligned(workspace, 16)) return MXQ_ERR_ALIGNMENT;
   int64_t total = 0;
   for (int g = 0; g < n_groups; ++g) {
     mxq_status st = gemm_checks(a, &w_groups[g], lr_u, ld_u, lr_l2t, lr_rank, out, ld_out, n_out);
@@ -257,7 +260,7 @@ mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int
     const mxq_qtensor* w = &w_groups[g];
     if (w->rows > 0) {
       hipError_t e = gemm_launch(a, w, w_perm + off, lr_u, ld_u, lr_l2t, lr_rank, bias, out,
-                                 ld_out, n_out, as_stream(stream));
+                                 ld_out, n_out, workspace, ws_bytes, as_stream(stream));
       if (e != hipSuccess) return MXQ_ERR_LAUNCH;
     }
     off += w->rows;

@@ -35,6 +35,8 @@ struct DqParams {
   GemmP g;
   const float* a_gp;   // NVFP4 tensor scale of a
   const float* w_gp;   // NVFP4 tensor scale of w
+  float* part;         // split K: fp32 partial sums [splits][M][N], else null
+  int kt_split;        // K-tiles per split (blockIdx.y selects the split)
 };
 
 __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
@@ -171,7 +173,9 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, half = lane >> 5;
-  const int KT = p.K / BK;
+  // this workgroup's K-tiles: all of them, or one split's share
+  const int kt0 = dp.part ? blockIdx.y * dp.kt_split : 0;
+  const int KT = dp.part ? min(p.K / BK, kt0 + dp.kt_split) : p.K / BK;
 
   const int fr = tid >> 1, fc = tid & 1;      // 4-bit operands: row, 32-element chunk
   Fp4Loader<WK> wl;
@@ -272,11 +276,11 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
       tot[i][j] = v16f{};
     }
 
-  gload(0);
+  gload(kt0);
   lstore(0);
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
+  for (int kt = kt0; kt < KT; ++kt) {
+    const int buf = (kt - kt0) & 1;
     if constexpr (I4) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) sw[j] = nsw[j];
@@ -322,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[ks][i], bf[ks][j], acc[i][j]);
     }
-    if ((kt + 1) % kSlabTiles == 0) {
+    if ((kt - kt0 + 1) % kSlabTiles == 0) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -338,10 +342,49 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] += tot[i][j];
+  if (dp.part) {
+    // split K: this split's fp32 sums (C layout: lane column l32, rows
+    // 8(q/4) + 4*half + q%4 of each 32x32 tile); dq_reduce_kernel finishes
+    float* part = dp.part + (int64_t)blockIdx.y * p.M * p.N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + l32;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = m0 + wm * 64 + i * 32 + 8 * (q / 4) + 4 * half + q % 4;
+          if (row < p.M) part[(int64_t)row * p.N + n] = acc[i][j][q];
+        }
+    }
+    return;
+  }
   float alpha = 1.0f;
   if constexpr (AK == K_NV) alpha *= *dp.a_gp;
   if constexpr (WK == K_NV) alpha *= *dp.w_gp;
   epilogue<LR>(p, acc, alpha, m0, n0, wm, wn, lane);
+}
+
+// Split-K finish: y = RN_bf16(alpha * sum over splits (in split order) +
+// bias), stored through the column map.  One thread per output element.
+__global__ __launch_bounds__(kThreads) void dq_reduce_kernel(const float* part, int splits, int M,
+                                                           int N, const float* a_gp,
+                                                           const int32_t* col_map,
+                                                           const uint16_t* bias, uint16_t* out,
+                                                           int64_t ld_out, int n_out) {
+  const float alpha = a_gp ? *a_gp : 1.0f;
+  const int64_t total = (int64_t)M * N;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int row = (int)(e / N), n = (int)(e % N);
+    const int c = col_map ? col_map[n] : n;
+    if (c < 0 || c >= n_out) continue;
+    float sum = 0.f;
+    for (int sp = 0; sp < splits; ++sp) sum += part[(int64_t)sp * total + e];
+    const float v = alpha * sum + (bias ? bf16_bits_to_f32(bias[c]) : 0.f);
+    out[(int64_t)row * ld_out + c] = (uint16_t)f32_to_bf16_bits(v);
+  }
 }
 
 
@@ -349,6 +392,14 @@ template <int AK, int WK>
 hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
   if (lr) gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
   else gemm_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !p.part) return e;
+  const GemmP& g = p.g;
+  const int64_t total = (int64_t)g.M * g.N;
+  const int blocks = (int)((total + kThreads - 1) / kThreads < 4096 ? (total + kThreads - 1) / kThreads : 4096);
+  dq_reduce_kernel<<<blocks, kThreads, 0, s>>>(p.part, (int)grid.y, g.M, g.N,
+                                               AK == K_NV ? p.a_gp : nullptr, g.col_map, g.bias,
+                                               g.out, g.ld_out, g.n_out);
   return hipGetLastError();
 }
 
@@ -359,6 +410,18 @@ hipError_t dispatch_w(int w_fmt, bool lr, dim3 grid, const DqParams& p, hipStrea
 }
 
 }  // namespace
+
+int dq_splits(int64_t M, int64_t N) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles <= 0 || tiles > 128) return 1;
+  const int64_t s = 256 / tiles;
+  return (int)(s > 4 ? 4 : s);
+}
+
+int64_t gemm_dq_workspace(int64_t M, int64_t N) {
+  const int s = dq_splits(M, N);
+  return s > 1 ? (int64_t)s * M * N * 4 : 0;
+}
 
 hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s) {
   DqParams dp;
@@ -374,8 +437,19 @@ hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s) {
   p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
   dp.a_gp = a.a_g;
   dp.w_gp = a.w_g;
-  const dim3 grid(p.tiles_m * p.tiles_n);
+  dp.part = nullptr;
+  dp.kt_split = 0;
   const bool lr = a.rank > 0;
+  // Too few tiles to fill the chip (narrow weight groups): split K over
+  // blockIdx.y into fp32 partials in the workspace, then sum them in split
+  // order (deterministic) in a second kernel.  Not with the low-rank branch.
+  const int splits = lr ? 1 : dq_splits(a.M, a.N);
+  if (splits > 1 && a.ws && a.ws_bytes >= gemm_dq_workspace(a.M, a.N)) {
+    const int kt = (int)(a.K / BK);
+    dp.kt_split = (kt + splits - 1) / splits;
+    dp.part = a.ws;
+  }
+  const dim3 grid(p.tiles_m * p.tiles_n, dp.part ? (unsigned)((a.K / BK + dp.kt_split - 1) / dp.kt_split) : 1u);
   switch (a.a_fmt) {
     case FMT_NVFP4: return dispatch_w<K_NV>(a.w_fmt, lr, grid, dp, s);
     case FMT_MXFP8: return dispatch_w<K_MX8>(a.w_fmt, lr, grid, dp, s);

@@ -53,8 +53,13 @@ struct GemmArgs {
   int rank;
   const uint16_t* bias;    // bf16 [n_out]
   uint16_t* out; int64_t ld_out; int64_t n_out;
+  float* ws; int64_t ws_bytes;   // optional workspace (INT4-row split K)
 };
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s);
+// INT4-row route: K splits for an M x N problem (1 = none) and the
+// workspace bytes they need.
+int dq_splits(int64_t M, int64_t N);
+int64_t gemm_dq_workspace(int64_t M, int64_t N);
 hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_dqp(const GemmArgs& a, hipStream_t s);
 

@@ -163,6 +163,14 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
  *              output column; lr_rank 0 = off, else a multiple of 16 <= 128.
  *  bias        optional device bf16 [n_out], indexed by output column.
  *  out         device bf16 [M][ld_out], n_out columns; 4-byte aligned.
+ *  workspace   optional (NULL, or 16-byte aligned device memory of ws_bytes):
+ *              with at least mxq_workspace_size(MXQ_OP_GEMM, M, N, w->fmt)
+ *              bytes, INT4 weights too narrow to fill the GPU (few output
+ *              tiles) split K into fp32 partial sums there, which a second
+ *              kernel adds in a fixed order (results are deterministic; they
+ *              may differ from the unsplit sum by fp32 rounding, within the
+ *              same error bound).  Otherwise, and for every other route and
+ *              with a low-rank branch, it is unused.
  * Requirements: a->cols == w->cols == K, K a multiple of 128.
  * M or N of 0 is a no-op.  Accumulation is fp32; long K is summed in slabs.
  */
@@ -178,7 +186,8 @@ mxq_status mxq_gemm(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* w
  * order; w_perm (device int32, sum of group rows) gives each grouped row's
  * output column, group after group.  Each group runs mxq_gemm's route for
  * its format on the same stream; the low-rank branch and bias, if given,
- * are added exactly once per output column.
+ * are added exactly once per output column.  The workspace is mxq_gemm's,
+ * shared by the groups in turn (size it for the largest INT4 group).
  */
 mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int32_t n_groups,
                           const int32_t* w_perm,
@@ -225,7 +234,9 @@ int32_t mxq_act_format_for_step(const uint8_t* table, int32_t n_layers, int32_t 
 enum { MXQ_OP_QUANTIZE = 1, MXQ_OP_GEMM = 2, MXQ_OP_SELECT = 3 };
 
 /* Workspace bytes an operation needs for a [rows, cols] operand of format
- * fmt (0 when none); returns -1 for unknown arguments.  Host-only. */
+ * fmt (0 when none); for MXQ_OP_GEMM rows = M, cols = N (weight rows) and
+ * fmt = the weight format (the optional split-K workspace).  Returns -1 for
+ * unknown arguments.  Host-only. */
 int64_t mxq_workspace_size(int32_t op, int64_t rows, int64_t cols, int32_t fmt);
 
 /* Per-row storage of a format with cols elements per row: code bytes and

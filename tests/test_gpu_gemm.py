@@ -145,3 +145,38 @@ def test_gemm_dq_tiles(fa, fw, m, n, k):
     ratio = gu.check_gemm(y, a_deq, gu.dequant_w_for_gemm(qw), gu.alpha_of(qa, qw), rows=rows,
                           tag=f"{fa}x{fw} tiles {m}x{n}x{k}")
     gu.say(f"  worst err/tol {ratio:.3g}")
+
+
+@pytest.mark.parametrize("fa", ["MXFP8", "NVFP4", "MXFP4"])
+def test_int4_split_k(fa):
+    """Narrow INT4 weight groups (few output tiles) split K into fp32 partial
+    sums when a workspace is given, summed in a fixed order by a second
+    kernel with the alpha, bias and column map of the epilogue.  Both paths
+    meet the tolerance; the split one is deterministic.  K = 4224 gives 66
+    K-tiles of 64 over four splits (17, 17, 17, 15), each with its own fp32
+    slabs."""
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    m, n, k = 300, 20, 4224
+    gu.say(f"gemm {fa}xINT4 split K M={m} N={n} K={k}")
+    qa, qw = _operands(m, n, k, fa, "INT4", seed=77)
+    a_dev, w_dev = gu.qtensor_from_oracle(qa, m, k), gu.qtensor_from_oracle(qw, n, k)
+    assert mxq.workspace_size(mxq.OP_GEMM, m, n, mxq.INT4) == 4 * m * n * 4
+    rng = np.random.default_rng(9)
+    n_out = 40
+    perm = rng.permutation(n_out)[:n].astype(np.int32)
+    bias = wl.bf16_to_f32(wl.f32_to_bf16_bits(rng.normal(0, 1, n_out).astype(np.float32)))
+    bias_dev = gu.to_dev_bf16(wl.f32_to_bf16_bits(bias))
+    perm_dev = torch.from_numpy(perm).cuda()
+    ys = []
+    for ws in (False, None, None):
+        out = torch.full((m, n_out), -7.0, dtype=torch.bfloat16, device="cuda")
+        ys.append(mxq.gemm(a_dev, w_dev, n_out=n_out, w_out_col=perm_dev, bias=bias_dev, out=out,
+                           workspace=ws))
+    a_deq, w_deq = gu.dequant_a_for_gemm(qa), gu.dequant_w_for_gemm(qw)
+    alpha = gu.alpha_of(qa, qw)
+    untouched = np.setdiff1d(np.arange(n_out), perm)
+    for y, tag in zip(ys, ("unsplit", "split", "split again")):
+        assert np.all(y.float().cpu().numpy()[:, untouched] == -7.0)
+        gu.check_gemm(y, a_deq, w_deq, alpha, bias=bias[perm], cols=perm, tag=f"{fa}xINT4 {tag}")
+    assert torch.equal(ys[1], ys[2])
