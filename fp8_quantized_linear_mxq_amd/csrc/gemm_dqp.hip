@@ -12,9 +12,9 @@
 // tensor scales multiply the accumulator in the epilogue.
 //
 // Organisation (the same pipeline as the MXFP4 kernel):
-//  * workgroup tile (64*TM) x (64*TN), four waves in a 2 x 2 grid, each
-//    wave (32*TM) x (32*TN): every dequantized fragment feeds TN (activation)
-//    or TM (weight) MFMAs;
+//  * workgroup tile (32*TM*WGM) x (64*TN), 2*WGM waves in a WGM x 2 grid
+//    (four, or eight for 256-row tiles), each wave (32*TM) x (32*TN): every
+//    dequantized fragment feeds TN (activation) or TM (weight) MFMAs;
 //  * raw code and scale tiles (4-bit codes are a quarter, 8-bit codes half
 //    the bytes of 16-bit tiles) stream into a 3-stage LDS ring with direct
 //    global->LDS loads two K-tiles ahead of the MFMAs;
@@ -127,18 +127,21 @@ __device__ __forceinline__ uint4 dq(const uint32_t* raw, int ks, const Scales<K,
   }
 }
 
-template <int AK, int WK, int TM, int TN, bool SLAB, bool LR>
-__global__ __launch_bounds__(kThreads, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpParams dp) {
+template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR>
+__global__ __launch_bounds__(128 * WGM, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpParams dp) {
   const GemmP& p = dp.g;
   constexpr bool FP16 = (AK == K_NV && WK == K_NV);
-  constexpr int TBM = 64 * TM, TBN = 64 * TN;
+  constexpr int NW = 2 * WGM;   // waves: WGM (rows) x 2 (columns)
+  constexpr int TBM = 32 * TM * WGM, TBN = 64 * TN;
   constexpr int A_RB = row_bytes<AK>(), W_RB = row_bytes<WK>();
   constexpr int A_CH = A_RB / 16, W_CH = W_RB / 16;
   constexpr int SBA = scale_bytes<AK>(), SBW = scale_bytes<WK>();
   constexpr int A_STAGE = TBM * A_RB, W_STAGE = TBN * W_RB;
-  constexpr int S_STAGE = scale_region_bytes<TBM, SBA, TBN, SBW>();
-  constexpr int STAGE = A_STAGE + W_STAGE + S_STAGE;
-  constexpr int NT = (TBM * A_CH + TBN * W_CH) / 256 + S_STAGE / 1024;   // loads per wave per K-tile
+  constexpr int S_STAGE = scale_region_bytes<TBM, SBA, TBN, SBW, NW>();
+  constexpr bool PAD = (TBM * A_CH / 64) % NW != 0 || (TBN * W_CH / 64) % NW != 0;
+  constexpr int STAGE = A_STAGE + W_STAGE + S_STAGE + (PAD ? 1024 : 0);
+  constexpr int NT = tile_loads<TBM, A_RB, NW>() + tile_loads<TBN, W_RB, NW>() +
+                     S_STAGE / (256 * NW);   // loads per wave per K-tile
   constexpr int A_DW = A_RB / 8, W_DW = W_RB / 8;   // dwords of a lane's run per K-tile
   static_assert(2 * NT < 64, "vmcnt range");
   // three separate arrays: reads of one stage are visibly independent of the
@@ -177,9 +180,11 @@ __global__ __launch_bounds__(kThreads, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpPar
   auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const bool past = kt >= KT;   // past the end of K: a tile of zeros
     kt = past ? KT - 1 : kt;
-    issue_tile<TBM, A_RB>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past);
-    issue_tile<TBN, W_RB>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past);
-    issue_scale_tile<TBM, SBA, TBN, SBW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane, past);
+    uint8_t* pad = st + A_STAGE + W_STAGE + S_STAGE;
+    issue_tile<TBM, A_RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad);
+    issue_tile<TBN, W_RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad);
+    issue_scale_tile<TBM, SBA, TBN, SBW, NW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane,
+                                             past);
   };
 
   v16f acc[TM][TN];
@@ -310,22 +315,23 @@ __global__ __launch_bounds__(kThreads, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpPar
   if constexpr (WK == K_NV) alpha *= *dp.w_gp;
   wait_lgkmcnt0();
   __syncthreads();
-  static_assert(2 * 32 * (TN * 64 + 16) <= STAGE, "two staging slices per stage");
-  uint8_t* region = (wave < 2 ? st0 : st1) + (wave & 1) * 32 * (TN * 64 + 16);
+  constexpr int RG = 32 * (TN * 64 + 16), SL = STAGE / RG;   // staging slices per stage
+  static_assert(3 * SL >= NW, "a staging slice per wave");
+  uint8_t* region = (wave / SL == 0 ? st0 : wave / SL == 1 ? st1 : st2) + (wave % SL) * RG;
   epilogue_tr<LR, TM, TN>(p, acc, alpha, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
 }
 
-template <int AK, int WK, int TM, int TN, bool SLAB>
+template <int AK, int WK, int TM, int TN, bool SLAB, int WGM = 2>
 hipError_t launch_cfg(bool lr, DqpParams dp, hipStream_t s) {
-  dp.g.tiles_m = (dp.g.M + 64 * TM - 1) / (64 * TM);
+  dp.g.tiles_m = (dp.g.M + 32 * TM * WGM - 1) / (32 * TM * WGM);
   dp.g.tiles_n = (dp.g.N + 64 * TN - 1) / (64 * TN);
   const int tiles = dp.g.tiles_m * dp.g.tiles_n;
   // tile-rows per group: one XCD's share (tiles / 8) as a near-square block
   dp.gm = 1;
   while (dp.gm * 2 <= dp.g.tiles_m && dp.gm * 2 * dp.gm * 2 <= (tiles + 7) / 8) dp.gm *= 2;
   const dim3 grid(tiles);
-  if (lr) gemm_dqp_kernel<AK, WK, TM, TN, SLAB, true><<<grid, kThreads, 0, s>>>(dp);
-  else gemm_dqp_kernel<AK, WK, TM, TN, SLAB, false><<<grid, kThreads, 0, s>>>(dp);
+  if (lr) gemm_dqp_kernel<AK, WK, TM, TN, WGM, SLAB, true><<<grid, 128 * WGM, 0, s>>>(dp);
+  else gemm_dqp_kernel<AK, WK, TM, TN, WGM, SLAB, false><<<grid, 128 * WGM, 0, s>>>(dp);
   return hipGetLastError();
 }
 
@@ -335,24 +341,29 @@ hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
   // past 32 K-tiles the fp32 chains are flushed into a second accumulator
   // every kSlab K-tiles, which only the small tile has the registers for
   if (dp.g.K / BK > 32) return launch_cfg<AK, WK, 2, 2, true>(lr, dp, s);
-  // Short K (under 16 K-tiles): 128x128 tiles, two workgroups per compute
-  // unit, so one tile's pipeline fill and output stores overlap the other's
-  // MFMAs.  Longer K: the 256-row tile that fills the 256 compute units in
-  // the fewest rounds per unit of work; ties go to the wider tile (fewer
-  // dequantizations per MFMA: 4096 x 12288 x 3072 NVFP4 runs 3-7% faster on
-  // 256 x 256 than on 256 x 192).
-  if (dp.g.K / BK < 16) return launch_cfg<AK, WK, 2, 2, false>(lr, dp, s);
+  // Costs in 64x64 output blocks per compute unit over whole rounds of the
+  // 256 compute units: the tile that fills them in the fewest rounds per
+  // unit of work.  256-row tiles run eight waves (two per SIMD, wave tiles
+  // 64 x 96 or 64 x 128); ties go to the wider tile (fewer dequantizations
+  // per MFMA).  Short K (under 16 K-tiles) also weighs 128x128 tiles at two
+  // workgroups per compute unit (a round of two tiles: 8 blocks), where one
+  // tile's pipeline fill and output stores overlap the other's MFMAs; ties
+  // go to them.
   const int64_t cu = 256;
-  auto rounds = [&](int64_t tbm, int64_t tbn) {
+  auto rounds = [&](int64_t tbm, int64_t tbn, int64_t slots) {
     const int64_t t = ((M + tbm - 1) / tbm) * ((N + tbn - 1) / tbn);
-    return (t + cu - 1) / cu;
+    return (t + cu * slots - 1) / (cu * slots);
   };
-  const int64_t c3 = rounds(256, 192) * 12, c2 = rounds(256, 128) * 8;
-  if constexpr (AK != K_MX8) {
-    const int64_t c4 = rounds(256, 256) * 16;
-    if (c4 <= c3 && c4 <= c2) return launch_cfg<AK, WK, 4, 4, false>(lr, dp, s);
+  const int64_t c4 = rounds(256, 256, 1) * 16, c3 = rounds(256, 192, 1) * 12;
+  if (dp.g.K / BK < 16) {
+    const int64_t c1 = rounds(128, 128, 2) * 8;
+    if (c4 < c1 && c4 <= c3) return launch_cfg<AK, WK, 2, 4, false, 4>(lr, dp, s);
+    if (c3 < c1) return launch_cfg<AK, WK, 2, 3, false, 4>(lr, dp, s);
+    return launch_cfg<AK, WK, 2, 2, false>(lr, dp, s);
   }
-  if (c3 <= c2) return launch_cfg<AK, WK, 4, 3, false>(lr, dp, s);
+  const int64_t c2 = rounds(256, 128, 1) * 8;
+  if (c4 <= c3 && c4 <= c2) return launch_cfg<AK, WK, 2, 4, false, 4>(lr, dp, s);
+  if (c3 <= c2) return launch_cfg<AK, WK, 2, 3, false, 4>(lr, dp, s);
   return launch_cfg<AK, WK, 4, 2, false>(lr, dp, s);
 }
 

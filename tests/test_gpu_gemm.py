@@ -124,10 +124,11 @@ def test_gemm_mx_tiles(m, n, k):
     gu.say(f"  worst err/tol {ratio:.3g}")
 
 
-# Long-K shapes that make the dequantizing route pick its 256-row workgroup
-# tiles (256x128; 256x192; 256x256 for 4-bit activations, 256x128 for 8-bit),
-# with ragged M and N tails; output rows are checked on a sample.
-DQ_TILE_SHAPES = [(2000, 2300, 2048), (4000, 2300, 2048), (4000, 4000, 2048)]
+# Shapes that make the dequantizing route pick its 256-row workgroup tiles:
+# 256x128 (four waves), 256x192 and 256x256 (eight waves) at K = 2048, and
+# 256x192 at a short K (9 K-tiles) where it fills whole rounds; ragged M and
+# N tails; output rows are checked on a sample.
+DQ_TILE_SHAPES = [(2000, 2300, 2048), (4000, 2300, 2048), (4000, 4000, 2048), (4096, 3072, 1152)]
 DQ_PAIRS = [(a, w) for a in ("MXFP8", "NVFP4", "MXFP4") for w in ("MXFP4", "NVFP4")
             if (a, w) != ("MXFP4", "MXFP4")]
 
