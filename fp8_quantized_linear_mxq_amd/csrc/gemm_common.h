@@ -119,4 +119,41 @@ __device__ __forceinline__ void epilogue(const GemmP& p, v16f acc[2][2], float a
   }
 }
 
+namespace {
+
+// Split-K finish: y = RN_bf16(alpha * sum over splits (in split order) +
+// bias), stored through the column map; part is [splits][M][N] fp32.  One
+// thread per output element.  (A copy per translation unit.)
+__global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* part, int splits,
+                                                               int M, int N, const float* a_gp,
+                                                               const int32_t* col_map,
+                                                               const uint16_t* bias,
+                                                               uint16_t* out, int64_t ld_out,
+                                                               int n_out) {
+  const float alpha = a_gp ? *a_gp : 1.0f;
+  const int64_t total = (int64_t)M * N;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int row = (int)(e / N), n = (int)(e % N);
+    const int c = col_map ? col_map[n] : n;
+    if (c < 0 || c >= n_out) continue;
+    float sum = 0.f;
+    for (int sp = 0; sp < splits; ++sp) sum += part[(int64_t)sp * total + e];
+    const float v = alpha * sum + (bias ? bf16_bits_to_f32(bias[c]) : 0.f);
+    out[(int64_t)row * ld_out + c] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+inline hipError_t launch_splitk_reduce(const GemmP& g, const float* part, int splits,
+                                       const float* alpha, hipStream_t s) {
+  const int64_t total = (int64_t)g.M * g.N;
+  const int64_t want = (total + kThreads - 1) / kThreads;
+  const int blocks = (int)(want < 4096 ? want : 4096);
+  splitk_reduce_kernel<<<blocks, kThreads, 0, s>>>(part, splits, g.M, g.N, alpha, g.col_map,
+                                                   g.bias, g.out, g.ld_out, g.n_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 }  // namespace mxq

@@ -344,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
     for (int j = 0; j < 2; ++j) acc[i][j] += tot[i][j];
   if (dp.part) {
     // split K: this split's fp32 sums (C layout: lane column l32, rows
-    // 8(q/4) + 4*half + q%4 of each 32x32 tile); dq_reduce_kernel finishes
+    // 8(q/4) + 4*half + q%4 of each 32x32 tile); launch_splitk_reduce finishes
     float* part = dp.part + (int64_t)blockIdx.y * p.M * p.N;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -366,41 +366,13 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
   epilogue<LR>(p, acc, alpha, m0, n0, wm, wn, lane);
 }
 
-// Split-K finish: y = RN_bf16(alpha * sum over splits (in split order) +
-// bias), stored through the column map.  One thread per output element.
-__global__ __launch_bounds__(kThreads) void dq_reduce_kernel(const float* part, int splits, int M,
-                                                           int N, const float* a_gp,
-                                                           const int32_t* col_map,
-                                                           const uint16_t* bias, uint16_t* out,
-                                                           int64_t ld_out, int n_out) {
-  const float alpha = a_gp ? *a_gp : 1.0f;
-  const int64_t total = (int64_t)M * N;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int row = (int)(e / N), n = (int)(e % N);
-    const int c = col_map ? col_map[n] : n;
-    if (c < 0 || c >= n_out) continue;
-    float sum = 0.f;
-    for (int sp = 0; sp < splits; ++sp) sum += part[(int64_t)sp * total + e];
-    const float v = alpha * sum + (bias ? bf16_bits_to_f32(bias[c]) : 0.f);
-    out[(int64_t)row * ld_out + c] = (uint16_t)f32_to_bf16_bits(v);
-  }
-}
-
-
 template <int AK, int WK>
 hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
   if (lr) gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
   else gemm_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.part) return e;
-  const GemmP& g = p.g;
-  const int64_t total = (int64_t)g.M * g.N;
-  const int blocks = (int)((total + kThreads - 1) / kThreads < 4096 ? (total + kThreads - 1) / kThreads : 4096);
-  dq_reduce_kernel<<<blocks, kThreads, 0, s>>>(p.part, (int)grid.y, g.M, g.N,
-                                               AK == K_NV ? p.a_gp : nullptr, g.col_map, g.bias,
-                                               g.out, g.ld_out, g.n_out);
-  return hipGetLastError();
+  return launch_splitk_reduce(p.g, p.part, (int)grid.y, AK == K_NV ? p.a_gp : nullptr, s);
 }
 
 template <int AK>
