@@ -125,8 +125,11 @@ __device__ __forceinline__ void e2m1_thresholds_f64(double d, float u[7]) {
 // (Fast2Sum, |t_hi| >= |e|), |r| <= half an ulp of u: the smallest float32
 // >= t (odd i) is u unless r > 0, the smallest > t (even i) u unless r >= 0.
 // Valid while every residual is a normal float32; smaller d (below 2**-60)
-// takes the float64 path.
+// takes the float64 path.  Every product and sum here must round on its own:
+// a multiply fused into a later add (t_hi into n or into n - t_hi) breaks the
+// error-free steps, so contraction is off in this function.
 __device__ __forceinline__ void e2m1_thresholds_sg(float s, float g, float u[7]) {
+#pragma clang fp contract(off)
   const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
   const float d_hi = s * g;
   if (!(d_hi >= 0x1p-60f)) {          // zero, or close enough to underflow

@@ -145,3 +145,29 @@ def test_nvfp4_small_tensor_scales(exp2):
     assert float(q.tensor_scale.cpu()[0]) == float(want["g"])
     assert np.array_equal(gu.dev_scales(q, "NVFP4"), want["scales"])
     assert np.array_equal(gu.unpack_dev_codes(q, "NVFP4"), want["codes"])
+
+
+def test_nvfp4_thresholds_just_above_a_midpoint():
+    """Values a hair above a rounding midpoint of x / (s g): 75 / (18 g) is
+    3.5 + 1e-8 for g = 1.1904761791229248, so it must round up to 4.  The
+    threshold 3.5 * s * g is not a float32 and the float32 just above it is
+    75 itself, which the encoder finds only if each step of its error-free
+    threshold arithmetic rounds on its own (a multiply fused into a later add
+    moved these thresholds one ulp up)."""
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    g = np.float32(1.1904761791229248)
+    x = np.zeros((2, 32), np.float32)
+    x[0, :5] = [128.0, 75.0, -75.0, 37.5, -37.5]      # s = 18: 3.5+ and 1.75+
+    x[0, 16:19] = [64.0, 18.75, -18.75]                # s = 9: 1.75+
+    x[1, :3] = [107.0, 62.5, -62.5]                    # s = 15: 3.5+
+    x[1, 16:19] = [424.0, 125.0, -125.0]               # s = 60: 1.75+
+    gu.say("NVFP4 values just above a midpoint (static g)")
+    gd = torch.tensor([g], dtype=torch.float32).cuda()
+    want = oq.quantize(x, "NVFP4", tensor_scale=g)
+    assert want["codes"][0, 1] == 6 and want["codes"][1, 17] == 4   # 4.0 and 2.0: rounded up
+    for dtype in ("f32", "bf16"):
+        xd = gu.act_to_dev(wl.f32_to_bf16_bits(x) if dtype == "bf16" else x, dtype)
+        q = mxq.quantize(xd, mxq.NVFP4, static_tensor_scale=gd)
+        assert np.array_equal(gu.dev_scales(q, "NVFP4"), want["scales"])
+        assert np.array_equal(gu.unpack_dev_codes(q, "NVFP4"), want["codes"]), dtype
