@@ -55,13 +55,15 @@ def gemm_dtype(act_fmt: str, w_fmt: str) -> str:
     return "bf16"
 
 
-def quantize_bytes(w: wl.Workload) -> int:
+def quantize_bytes(w: wl.Workload, cols: int | None = None) -> int:
     """Algorithmic HBM bytes of one activation quantize: read x, write codes
-    and scales (and u for the low-rank branch)."""
+    and scales (and u for the low-rank branch).  ``cols``: the quantized
+    width when it is not K (the convolution's input channels)."""
     esz = 2 if w.act_dtype == "bf16" else 4
-    rd = w.m * w.k * esz
-    code = w.m * w.k // (1 if w.act_fmt == "MXFP8" else 2)
-    scale = w.m * w.k // (16 if w.act_fmt == "NVFP4" else 32)
+    k = w.k if cols is None else cols
+    rd = w.m * k * esz
+    code = w.m * k // (1 if w.act_fmt == "MXFP8" else 2)
+    scale = w.m * k // (16 if w.act_fmt == "NVFP4" else 32)
     wr = code + scale + (w.m * w.rank * 4 if w.rank else 0)
     if w.act_fmt == "NVFP4":
         rd *= 2            # the dynamic tensor scale needs a first pass over x
@@ -85,17 +87,22 @@ def mixed_weights(w: wl.Workload, mxq, torch):
     return groups, perm, cnt
 
 
-def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None):
-    """Device buffer sets: activations, pre-quantized weights, outputs."""
+def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None, conv="implicit"):
+    """Device buffer sets: activations, pre-quantized weights, outputs.  The
+    convolution layer's activations are the input's pixel rows (implicit
+    im2col) or the explicit im2col matrix."""
     if w.w_fmt == "MIXED":
-        act = wl.im2col(wl.conv_latent(w))
-        x0 = torch.from_numpy(act.view(np.int16)).view(torch.bfloat16).cuda()
-        del act
+        lat = wl.conv_latent(w)
+        act = lat.reshape(-1, lat.shape[2]) if conv == "implicit" else wl.im2col(lat)
+        x0 = torch.from_numpy(np.ascontiguousarray(act).view(np.int16)).view(torch.bfloat16).cuda()
+        del act, lat
         groups, perm, _ = mixed
+        ws_n = max([mxq.workspace_size(mxq.OP_GEMM, w.m, g.rows, g.fmt) for g in groups] + [16])
         sets = []
         for i in range(n_sets):
             sets.append(dict(x=x0 if i == 0 else x0.clone(), groups=groups, perm=perm,
-                             qa=mxq.empty_qtensor(mxq.MXFP8, w.m, w.k),
+                             qa=mxq.empty_qtensor(mxq.MXFP8, w.m, x0.shape[1]),
+                             ws=torch.empty((ws_n,), dtype=torch.uint8, device="cuda"),
                              out=torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")))
         torch.cuda.synchronize()
         return sets
@@ -229,6 +236,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--conv", default="implicit", choices=["implicit", "im2col"],
+                    help="convolution layer: gather the taps inside the GEMM from the "
+                         "quantized input (implicit) or quantize the explicit im2col matrix")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -243,10 +253,13 @@ def main() -> int:
     mxq.load()
     torch.cuda.set_device(0)
     mixed = mixed_weights(w, mxq, torch) if w.w_fmt == "MIXED" else None
-    one = make_sets(w, 1, mxq, torch, mixed)
+    one = make_sets(w, 1, mxq, torch, mixed, args.conv)
     per_set = set_bytes(one[0])
     n_sets = max(2, int(np.ceil(512e6 / per_set)) + 1)
-    sets = one + make_sets(w, n_sets - 1, mxq, torch, mixed)
+    sets = one + make_sets(w, n_sets - 1, mxq, torch, mixed, args.conv)
+    implicit = mixed is not None and args.conv == "implicit"
+    if implicit:
+        lat_h, lat_w, lat_c = w.extra["latent"]
     fa = wl_fmt(mxq, w.act_fmt)
 
     def quant(s):
@@ -257,8 +270,12 @@ def main() -> int:
                          workspace=s["ws"])
 
     def gemm(s):
-        if mixed:
-            mxq.gemm_mixed(s["qa"], s["groups"], s["perm"], w.n, out=s["out"])
+        if implicit:
+            mxq.conv3x3_gemm_mixed(s["qa"], lat_h, lat_w, s["groups"], s["perm"], w.n,
+                                   out=s["out"], workspace=s["ws"])
+        elif mixed:
+            mxq.gemm_mixed(s["qa"], s["groups"], s["perm"], w.n, out=s["out"],
+                           workspace=s["ws"])
         else:
             mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"])
 
@@ -299,7 +316,7 @@ def main() -> int:
         ent = t.get(w.name)
         if ent and ent.get("kernel_source_digest") == kernel_source_digest():
             traffic = ent.get("gemm_hbm_bytes_per_launch")
-    qbytes = quantize_bytes(w)
+    qbytes = quantize_bytes(w, lat_c if implicit else None)
     rec = {
         "metric": "block-scaled GEMM TFLOP/s & % MXFP4 peak; quantize GB/s & % HBM BW",
         "value": round(2.0 * w.m * w.n * w.k / (ms * 1e-3) / 1e12, 2),
@@ -330,6 +347,9 @@ def main() -> int:
     if mixed:
         rec["config"]["weight_groups"] = {"INT4": mixed[2][0], "MXFP4": mixed[2][1],
                                           "NVFP4": mixed[2][2]}
+        rec["config"]["conv"] = ("implicit im2col: quantize the 128x128x2560 input once, "
+                                 "gather the 3x3 taps in the GEMM") if implicit else \
+            "explicit im2col: quantize the 16384x23040 matrix"
     if not args.no_cpu_baseline and not mixed:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)

@@ -25,7 +25,8 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARG", 2: "MXQ_ERR_UNSUPPORTED",
           6: "MXQ_ERR_NO_DEVICE", 7: "MXQ_ERR_LAUNCH"}
 
 # Every symbol include/mxq.h declares.
-EXPORTS = ("mxq_quantize", "mxq_gemm", "mxq_gemm_mixed", "mxq_select_format",
+EXPORTS = ("mxq_quantize", "mxq_gemm", "mxq_gemm_mixed", "mxq_conv3x3_gemm_mixed",
+           "mxq_select_format",
            "mxq_act_format_for_step", "mxq_workspace_size", "mxq_storage",
            "mxq_status_string", "mxq_version")
 
@@ -68,6 +69,9 @@ def load():
     lib.mxq_gemm.restype = i32
     lib.mxq_gemm_mixed.argtypes = [qp, qp, i32, vp, vp, i64, vp, i32, vp, vp, i64, i64, vp, sz, vp]
     lib.mxq_gemm_mixed.restype = i32
+    lib.mxq_conv3x3_gemm_mixed.argtypes = [qp, i64, i64, qp, i32, vp, vp, vp, i64, i64, vp, sz,
+                                           vp]
+    lib.mxq_conv3x3_gemm_mixed.restype = i32
     lib.mxq_select_format.argtypes = [vp, i32, i64, i64, i64, C.POINTER(i32), i32, vp, vp, vp,
                                       vp, vp, vp, sz, vp]
     lib.mxq_select_format.restype = i32
@@ -223,6 +227,25 @@ def gemm_mixed(a: QTensor, groups: list, w_perm, n_out: int, u=None, l2t=None, b
                             0 if u is None else u.stride(0), _ptr(l2t), rank, _ptr(bias),
                             _ptr(out), out.stride(0), n_out, wsp, wsn, _stream(stream))
     _check("mxq_gemm_mixed", st)
+    return out
+
+
+def conv3x3_gemm_mixed(x: QTensor, height: int, width: int, groups: list, w_perm, n_out: int,
+                       bias=None, out=None, stream=None, workspace=None):
+    """mxq_conv3x3_gemm_mixed: the 3x3 convolution (stride 1, zero padding 1)
+    of the quantized pixel rows ``x`` ([images*height*width, C]) with weight
+    groups of 9*C columns; returns the bf16 [x.rows, n_out] output tensor."""
+    import torch
+    lib = load()
+    if out is None:
+        out = torch.empty((x.rows, n_out), dtype=torch.bfloat16, device=x.codes.device)
+    xc = x.c()
+    arr = (QTensorC * len(groups))(*[g.c() for g in groups])
+    wsp, wsn = _gemm_workspace(x, groups, workspace)
+    st = lib.mxq_conv3x3_gemm_mixed(C.byref(xc), height, width, arr, len(groups), _ptr(w_perm),
+                                    _ptr(bias), _ptr(out), out.stride(0), n_out, wsp, wsn,
+                                    _stream(stream))
+    _check("mxq_conv3x3_gemm_mixed", st)
     return out
 
 

@@ -188,11 +188,18 @@ static mxq_status gemm_checks(const mxq_qtensor* a, const mxq_qtensor* w, const 
   return MXQ_OK;
 }
 
+// One GEMM launch of the route for (a->fmt, w->fmt).  With cv_c > 0 the
+// activation operand is the implicit im2col of a 3x3 convolution over an
+// [images * cv_h * cv_w][cv_c] pixel-row input (K = w->cols = 9 * cv_c).
 static hipError_t gemm_launch(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* col_map,
                               const float* lr_u, int64_t ld_u, const void* lr_l2t,
                               int32_t lr_rank, const void* bias, void* out, int64_t ld_out,
-                              int64_t n_out, void* workspace, size_t ws_bytes, hipStream_t s) {
+                              int64_t n_out, void* workspace, size_t ws_bytes, hipStream_t s,
+                              int64_t cv_h = 0, int64_t cv_w = 0, int64_t cv_c = 0) {
   GemmArgs g;
+  g.cv_h = cv_h;
+  g.cv_w = cv_w;
+  g.cv_c = cv_c;
   g.ws = static_cast<float*>(workspace);
   g.ws_bytes = workspace ? (int64_t)ws_bytes : 0;
   g.a_fmt = a->fmt;
@@ -209,7 +216,7 @@ static hipError_t gemm_launch(const mxq_qtensor* a, const mxq_qtensor* w, const 
   g.w_g = w->tensor_scale;
   g.M = a->rows;
   g.N = w->rows;
-  g.K = a->cols;
+  g.K = w->cols;
   g.col_map = col_map;
   g.u = lr_u;
   g.ld_u = ld_u;
@@ -261,6 +268,54 @@ mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int
     if (w->rows > 0) {
       hipError_t e = gemm_launch(a, w, w_perm + off, lr_u, ld_u, lr_l2t, lr_rank, bias, out,
                                  ld_out, n_out, workspace, ws_bytes, as_stream(stream));
+      if (e != hipSuccess) return MXQ_ERR_LAUNCH;
+    }
+    off += w->rows;
+  }
+  return MXQ_OK;
+}
+
+mxq_status mxq_conv3x3_gemm_mixed(const mxq_qtensor* x, int64_t height, int64_t width,
+                                  const mxq_qtensor* w_groups, int32_t n_groups,
+                                  const int32_t* w_perm, const void* bias, void* out,
+                                  int64_t ld_out, int64_t n_out, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  if (!w_groups || n_groups <= 0 || n_groups > 8) return MXQ_ERR_INVALID_ARG;
+  mxq_status st = check_qtensor(x);
+  if (st != MXQ_OK) return st;
+  if (height <= 0 || width <= 0 || n_out < 0) return MXQ_ERR_INVALID_ARG;
+  if (x->fmt == MXQ_FMT_INT4) return MXQ_ERR_UNSUPPORTED;
+  if (workspace && !aligned(workspace, 16)) return MXQ_ERR_ALIGNMENT;
+  if (height > INT32_MAX / width) return MXQ_ERR_SHAPE;
+  const int64_t C = x->cols, hw = height * width;
+  // a K-tile (128) never spans two taps; pixels are whole images
+  if (C % 128 || x->rows % hw) return MXQ_ERR_SHAPE;
+  if (x->rows > INT32_MAX || 9 * C > INT32_MAX || n_out > INT32_MAX) return MXQ_ERR_SHAPE;
+  int64_t total = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    const mxq_qtensor* w = &w_groups[g];
+    st = check_qtensor(w);
+    if (st != MXQ_OK) return st;
+    if (w->fmt == MXQ_FMT_MXFP8) return MXQ_ERR_UNSUPPORTED;
+    // the scaled-MFMA route (MXFP4 x MXFP4) reads no implicit im2col
+    if (x->fmt == MXQ_FMT_MXFP4 && w->fmt == MXQ_FMT_MXFP4 && w->rows > 0)
+      return MXQ_ERR_UNSUPPORTED;
+    if (w->cols != 9 * C) return MXQ_ERR_SHAPE;
+    if (w->rows > INT32_MAX) return MXQ_ERR_SHAPE;
+    total += w->rows;
+  }
+  if (x->rows == 0 || n_out == 0 || total == 0) return MXQ_OK;
+  if (!out || ld_out < n_out) return MXQ_ERR_INVALID_ARG;
+  if (!aligned(out, 2)) return MXQ_ERR_ALIGNMENT;
+  // without a permutation a single group's row j is output column j
+  if (!w_perm && (n_groups > 1 || total > n_out)) return MXQ_ERR_INVALID_ARG;
+  int64_t off = 0;
+  for (int g = 0; g < n_groups; ++g) {
+    const mxq_qtensor* w = &w_groups[g];
+    if (w->rows > 0) {
+      hipError_t e = gemm_launch(x, w, w_perm ? w_perm + off : nullptr, nullptr, 0, nullptr, 0,
+                                 bias, out, ld_out, n_out, workspace, ws_bytes,
+                                 as_stream(stream), height, width, C);
       if (e != hipSuccess) return MXQ_ERR_LAUNCH;
     }
     off += w->rows;

@@ -27,7 +27,44 @@ struct GemmP {
   const float* u; int64_t ld_u; const uint16_t* l2t; int rank;
   const uint16_t* bias;
   uint16_t* out; int64_t ld_out; int n_out;
+  // Implicit im2col of a 3x3, stride-1, zero-padded convolution when cv_c > 0:
+  // A's codes and scales are the input's [images * cv_h * cv_w][cv_c] pixel
+  // rows; GEMM row m is output pixel m (row-major image, y, x) and K index
+  // (ky*3 + kx)*cv_c + c reads channel c of input pixel (y + ky - 1,
+  // x + kx - 1), zero outside the image.  cv_c is a multiple of the K-tile,
+  // so a K-tile never spans two taps.
+  int cv_h, cv_w, cv_c;
 };
+
+// The tap of K-tile kt (bk elements wide) of an implicit-im2col operand: the
+// pixel offsets (dy, dx), the K-tile's index inside the channel row, and the
+// row shift dy * width + dx.
+struct ConvTap {
+  int dy, dx, kc, shift;
+};
+
+__device__ __forceinline__ ConvTap conv_tap(const GemmP& p, int kt, int bk) {
+  const int tiles = p.cv_c / bk;   // K-tiles per tap
+  const int tap = kt / tiles;
+  ConvTap t;
+  t.kc = kt - tap * tiles;
+  t.dy = tap / 3 - 1;
+  t.dx = tap - 3 * (tap / 3) - 1;
+  t.shift = t.dy * p.cv_w + t.dx;
+  return t;
+}
+
+// Pixel coordinates of GEMM row `row` of an implicit-im2col operand.
+__device__ __forceinline__ void conv_pixel(const GemmP& p, int row, int& y, int& x) {
+  const int hw = row % (p.cv_h * p.cv_w);
+  y = hw / p.cv_w;
+  x = hw - y * p.cv_w;
+}
+
+// Whether pixel (y, x) shifted by the tap lies inside the image.
+__device__ __forceinline__ bool conv_inside(const GemmP& p, const ConvTap& t, int y, int x) {
+  return (unsigned)(y + t.dy) < (unsigned)p.cv_h && (unsigned)(x + t.dx) < (unsigned)p.cv_w;
+}
 
 __device__ __forceinline__ int remap_tile(int bid, int total) {
   const int q = total >> 3, r = total & 7;

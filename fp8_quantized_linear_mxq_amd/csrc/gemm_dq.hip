@@ -148,6 +148,17 @@ struct Fp4Loader {
     if constexpr (KIND == K_NV) s = *reinterpret_cast<const uint32_t*>(scl + kt * 4);  // 4 x E4M3
     else if constexpr (KIND == K_MX4) s = scl[kt * 2 + fc];                            // E8M0
   }
+  // Implicit im2col: K-tile kc of the channel row of the pixel `shift` rows
+  // away, or zero codes and scales when that pixel is outside the image.
+  __device__ void load_conv(int kc, int64_t shift, int64_t ld, int64_t lds, bool in) {
+    r = (ok && in) ? *reinterpret_cast<const uint4*>(code + shift * ld + (int64_t)kc * 32)
+                   : make_uint4(0, 0, 0, 0);
+    const uint8_t* sp = in ? scl + shift * lds : scl;
+    uint32_t v = 0;
+    if constexpr (KIND == K_NV) v = *reinterpret_cast<const uint32_t*>(sp + kc * 4);
+    else if constexpr (KIND == K_MX4) v = sp[kc * 2 + fc];
+    s = in ? v : 0u;
+  }
   template <bool FP16>
   __device__ void convert(uint4 o[4]) const {
     if constexpr (KIND == K_NV) {
@@ -160,8 +171,8 @@ struct Fp4Loader {
   }
 };
 
-template <int AK, int WK, bool LR>
-__global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
+template <int AK, int WK, bool LR, bool CONV>
+__device__ __forceinline__ void dq_body(const DqParams& dp) {
   const GemmP& p = dp.g;
   constexpr bool FP16 = (AK == K_NV && WK == K_NV);
   constexpr bool I4 = (WK == K_I4);
@@ -200,6 +211,15 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
       a_scl8[i] = p.as + (int64_t)(a_ok8[i] ? m0 + ar8[i] : 0) * p.ldas;
     }
   }
+  // Implicit im2col: pixel coordinates of this thread's activation rows.
+  int cv_y[2] = {0, 0}, cv_x[2] = {0, 0};
+  if constexpr (CONV) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = AK == K_MX8 ? m0 + ar8[i] : m0 + fr;
+      conv_pixel(p, row < p.M ? row : 0, cv_y[i], cv_x[i]);
+    }
+  }
   // INT4 weights: this lane's output columns' fp32 block scales.
   const float* sw_row[2];
   float2 sw[2], nsw[2];
@@ -213,7 +233,24 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
 
   auto gload = [&](int kt) {
     wl.load(kt);
-    if constexpr (AK == K_MX8) {
+    if constexpr (CONV) {
+      const ConvTap tp = conv_tap(p, kt, BK);
+      if constexpr (AK == K_MX8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const bool in = conv_inside(p, tp, cv_y[i], cv_x[i]);
+          ra8[i] = (a_ok8[i] && in)
+                       ? *reinterpret_cast<const uint4*>(a_code8[i] + (int64_t)tp.shift * p.lda +
+                                                         (int64_t)tp.kc * 64)
+                       : make_uint4(0, 0, 0, 0);
+          const uint8_t* sp = in ? a_scl8[i] + (int64_t)tp.shift * p.ldas : a_scl8[i];
+          const uint32_t v = sp[tp.kc * 2 + (ac8[i] >> 1)];
+          ras8[i] = in ? v : 0u;
+        }
+      } else {
+        al.load_conv(tp.kc, tp.shift, p.lda, p.ldas, conv_inside(p, tp, cv_y[0], cv_x[0]));
+      }
+    } else if constexpr (AK == K_MX8) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         ra8[i] = a_ok8[i] ? *reinterpret_cast<const uint4*>(a_code8[i] + (int64_t)kt * 64)
@@ -366,9 +403,22 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
   epilogue<LR>(p, acc, alpha, m0, n0, wm, wn, lane);
 }
 
+template <int AK, int WK, bool LR>
+__global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
+  dq_body<AK, WK, LR, false>(dp);
+}
+
+// The same GEMM with the activation operand read as the implicit im2col of a
+// 3x3 convolution.
+template <int AK, int WK>
+__global__ __launch_bounds__(kThreads) void conv_dq_kernel(DqParams dp) {
+  dq_body<AK, WK, false, true>(dp);
+}
+
 template <int AK, int WK>
 hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
-  if (lr) gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
+  if (p.g.cv_c > 0) conv_dq_kernel<AK, WK><<<grid, kThreads, 0, s>>>(p);
+  else if (lr) gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
   else gemm_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.part) return e;
@@ -407,6 +457,7 @@ hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s) {
   p.u = a.u; p.ld_u = a.ld_u; p.l2t = a.l2t; p.rank = a.rank;
   p.bias = a.bias;
   p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
+  p.cv_h = (int)a.cv_h; p.cv_w = (int)a.cv_w; p.cv_c = (int)a.cv_c;
   dp.a_gp = a.a_g;
   dp.w_gp = a.w_g;
   dp.part = nullptr;

@@ -127,8 +127,8 @@ __device__ __forceinline__ uint4 dq(const uint32_t* raw, int ks, const Scales<K,
   }
 }
 
-template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR>
-__global__ __launch_bounds__(128 * WGM, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpParams dp) {
+template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR, bool CONV>
+__device__ __forceinline__ void dqp_body(const DqpParams& dp) {
   const GemmP& p = dp.g;
   constexpr bool FP16 = (AK == K_NV && WK == K_NV);
   constexpr int NW = 2 * WGM;   // waves: WGM (rows) x 2 (columns)
@@ -177,14 +177,87 @@ __global__ __launch_bounds__(128 * WGM, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpPa
   const uint32_t sw_base =
       A_STAGE + W_STAGE + TBM * SBA + (wn * 32 * TN + l32) * SBW + (SBW == 8 ? 4 * half : 0);
 
+  // Implicit im2col: the row address and pixel of each of this lane's
+  // activation code loads and activation scale loads, fixed for the whole
+  // loop (the lane-to-slot map of issue_tile / issue_scale_tile); each K-tile
+  // adds its tap's row shift and reads zeros where the shifted pixel lies
+  // outside the image.  Loads that carry no row of A never read.
+  constexpr int A_LD = tile_loads<TBM, A_RB, NW>();
+  constexpr int S_DA = TBM * SBA / 4, S_D = S_DA + TBN * SBW / 4;
+  constexpr int S_LD = (S_D + 64 * NW - 1) / (64 * NW);
+  const uint8_t* cv_code[CONV ? A_LD : 1];
+  int cv_y[CONV ? A_LD : 1], cv_x[CONV ? A_LD : 1];
+  const uint8_t* cv_scl[CONV ? S_LD : 1];
+  int cv_sy[CONV ? S_LD : 1], cv_sx[CONV ? S_LD : 1];
+  if constexpr (CONV) {
+    constexpr int TOTAL = TBM * A_CH / 64;
+#pragma unroll
+    for (int t = 0; t < A_LD; ++t) {
+      const int idx = t * NW + wave;
+      const bool real = (TOTAL % NW == 0) || idx < TOTAL;
+      const int L = (real ? idx : 0) * 64 + lane;
+      const int r = L / A_CH, lc = (L % A_CH) ^ swz<A_CH>(r);
+      const int grow = m0 + r < p.M ? m0 + r : p.M - 1;
+      cv_code[t] = p.a + (int64_t)grow * p.lda + lc * 16;
+      conv_pixel(p, grow, cv_y[t], cv_x[t]);
+      if (!real) cv_y[t] = -(1 << 24);
+    }
+#pragma unroll
+    for (int t = 0; t < S_LD; ++t) {
+      const int d = (t * NW + wave) * 64 + lane;
+      const int dd = d < S_DA ? d : 0;
+      const int grow = m0 + dd / (SBA / 4) < p.M ? m0 + dd / (SBA / 4) : p.M - 1;
+      cv_scl[t] = p.as + (int64_t)grow * p.ldas + (dd % (SBA / 4)) * 4;
+      conv_pixel(p, grow, cv_sy[t], cv_sx[t]);
+      if (d >= S_DA) cv_sy[t] = -(1 << 24);
+    }
+  }
+
   auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const bool past = kt >= KT;   // past the end of K: a tile of zeros
     kt = past ? KT - 1 : kt;
     uint8_t* pad = st + A_STAGE + W_STAGE + S_STAGE;
-    issue_tile<TBM, A_RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad);
-    issue_tile<TBN, W_RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad);
-    issue_scale_tile<TBM, SBA, TBN, SBW, NW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane,
-                                             past);
+    if constexpr (CONV) {
+      const ConvTap tp = conv_tap(p, kt, BK);
+      const int64_t off = (int64_t)tp.shift * p.lda + tp.kc * A_RB;
+      constexpr int TOTAL = TBM * A_CH / 64;
+#pragma unroll
+      for (int t = 0; t < A_LD; ++t) {
+        const int idx = t * NW + wave;
+        const bool real = (TOTAL % NW == 0) || idx < TOTAL;
+        const bool in = !past && conv_inside(p, tp, cv_y[t], cv_x[t]);
+        const uint8_t* src = in ? cv_code[t] + off : g_zero16;
+        uint8_t* dst = real ? st + idx * 64 * 16 : pad;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
+      }
+      issue_tile<TBN, W_RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad);
+      // scales: activation rows through the tap, weight rows as issue_scale_tile
+      const int64_t soff = (int64_t)tp.shift * p.ldas + tp.kc * SBA;
+      uint8_t* region = st + A_STAGE + W_STAGE;
+#pragma unroll
+      for (int t = 0; t < S_LD; ++t) {
+        const int slot0 = (t * NW + wave) * 64;
+        const int d = slot0 + lane;
+        const uint8_t* src;
+        if (d < S_DA) {
+          src = conv_inside(p, tp, cv_sy[t], cv_sx[t]) ? cv_scl[t] + soff : g_zero16;
+        } else if (d < S_D) {
+          const int e = d - S_DA;
+          int r = n0 + e / (SBW / 4);
+          r = r < p.N ? r : p.N - 1;
+          src = p.ws + (int64_t)r * p.ldws + kt * SBW + (e % (SBW / 4)) * 4;
+        } else {
+          src = g_zero16;
+        }
+        src = past ? g_zero16 : src;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + slot0 * 4), 4, 0, 0);
+      }
+    } else {
+      issue_tile<TBM, A_RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad);
+      issue_tile<TBN, W_RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad);
+      issue_scale_tile<TBM, SBA, TBN, SBW, NW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane,
+                                               past);
+    }
   };
 
   v16f acc[TM][TN];
@@ -321,6 +394,18 @@ __global__ __launch_bounds__(128 * WGM, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpPa
   epilogue_tr<LR, TM, TN>(p, acc, alpha, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
 }
 
+template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR>
+__global__ __launch_bounds__(128 * WGM, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpParams dp) {
+  dqp_body<AK, WK, TM, TN, WGM, SLAB, LR, false>(dp);
+}
+
+// The same GEMM with the activation operand read as the implicit im2col of a
+// 3x3 convolution (128x128 tiles, two workgroups per compute unit).
+template <int AK, int WK, bool SLAB>
+__global__ __launch_bounds__(256, 2) void conv_dqp_kernel(DqpParams dp) {
+  dqp_body<AK, WK, 2, 2, 2, SLAB, false, true>(dp);
+}
+
 template <int AK, int WK, int TM, int TN, bool SLAB, int WGM = 2>
 hipError_t launch_cfg(bool lr, DqpParams dp, hipStream_t s) {
   dp.g.tiles_m = (dp.g.M + 32 * TM * WGM - 1) / (32 * TM * WGM);
@@ -336,7 +421,21 @@ hipError_t launch_cfg(bool lr, DqpParams dp, hipStream_t s) {
 }
 
 template <int AK, int WK>
+hipError_t launch_conv(DqpParams dp, hipStream_t s) {
+  dp.g.tiles_m = (dp.g.M + 127) / 128;
+  dp.g.tiles_n = (dp.g.N + 127) / 128;
+  const int tiles = dp.g.tiles_m * dp.g.tiles_n;
+  dp.gm = 1;
+  while (dp.gm * 2 <= dp.g.tiles_m && dp.gm * 2 * dp.gm * 2 <= (tiles + 7) / 8) dp.gm *= 2;
+  // long K: fp32 slabs of kSlab K-tiles, as for the plain GEMM
+  if (dp.g.K / BK > 32) conv_dqp_kernel<AK, WK, true><<<tiles, 256, 0, s>>>(dp);
+  else conv_dqp_kernel<AK, WK, false><<<tiles, 256, 0, s>>>(dp);
+  return hipGetLastError();
+}
+
+template <int AK, int WK>
 hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
+  if (dp.g.cv_c > 0) return launch_conv<AK, WK>(dp, s);
   const int64_t M = dp.g.M, N = dp.g.N;
   // past 32 K-tiles the fp32 chains are flushed into a second accumulator
   // every kSlab K-tiles, which only the small tile has the registers for
@@ -386,6 +485,7 @@ hipError_t launch_gemm_dqp(const GemmArgs& a, hipStream_t s) {
   p.u = a.u; p.ld_u = a.ld_u; p.l2t = a.l2t; p.rank = a.rank;
   p.bias = a.bias;
   p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
+  p.cv_h = (int)a.cv_h; p.cv_w = (int)a.cv_w; p.cv_c = (int)a.cv_c;
   dp.a_gp = a.a_g;
   dp.w_gp = a.w_g;
   const bool lr = a.rank > 0;

@@ -304,6 +304,7 @@ hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s) {
   p.u = a.u; p.ld_u = a.ld_u; p.l2t = a.l2t; p.rank = a.rank;
   p.bias = a.bias;
   p.out = a.out; p.ld_out = a.ld_out; p.n_out = (int)a.n_out;
+  p.cv_h = (int)a.cv_h; p.cv_w = (int)a.cv_w; p.cv_c = (int)a.cv_c;
   const bool lr = a.rank > 0;
   if (a.K > 4096) return launch_cfg<2, 2, 2, true>(lr, p, s);
   // Large tiles move the fewest bytes per MFMA; pick the one whose tile count

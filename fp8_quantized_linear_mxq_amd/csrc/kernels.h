@@ -54,6 +54,9 @@ struct GemmArgs {
   const uint16_t* bias;    // bf16 [n_out]
   uint16_t* out; int64_t ld_out; int64_t n_out;
   float* ws; int64_t ws_bytes;   // optional workspace (INT4-row split K)
+  // implicit im2col of a 3x3 convolution (0 = plain GEMM): A is the input's
+  // [images * cv_h * cv_w][cv_c] pixel rows and K = 9 * cv_c
+  int64_t cv_h, cv_w, cv_c;
 };
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s);
 // INT4-row route: K splits for an M x N problem (1 = none) and the

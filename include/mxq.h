@@ -196,6 +196,39 @@ mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int
                           void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * mxq_conv3x3_gemm_mixed -- a 3x3, stride-1, zero-padding-1 convolution as the
+ * grouped mixed-format GEMM of mxq_gemm_mixed, with the activation operand
+ * read as the implicit im2col of the quantized input (Chameleon article,
+ * "routing" paragraph: the concatenated-feature convolutions, kept at MXFP8).
+ * No im2col matrix is built or quantized: each 32- or 16-block of an im2col
+ * row is either a block of one input pixel's channel row, which quantizes to
+ * the same codes and scale in the input, or lies wholly in the zero padding
+ * and adds nothing (and the NVFP4 tensor amax is the input's, since every
+ * pixel is some output's centre tap).
+ *
+ *  x           quantized input [images * height * width][C] (pixel rows in
+ *              row-major image, y, x order; C channels): MXFP8, NVFP4 or
+ *              MXFP4.  C must be a multiple of 128.
+ *  height, width  the spatial size of each image (> 0); x->rows must be a
+ *              multiple of height * width.
+ *  w_groups, n_groups, w_perm  weight groups as in mxq_gemm_mixed, each
+ *              [rows][9 * C] with K index (ky * 3 + kx) * C + c for tap
+ *              (ky, kx) and channel c.  w_perm may be NULL for one group
+ *              (row j writes output column j).  MXFP4 x MXFP4 groups are
+ *              MXQ_ERR_UNSUPPORTED (the scaled-MFMA route has no im2col
+ *              reader).
+ *  bias, out, ld_out, n_out, workspace  as in mxq_gemm_mixed; out row m is
+ *              output pixel m (same order as x).  No low-rank branch.
+ * Output pixel (y, x) with tap (ky, kx) reads input pixel (y + ky - 1,
+ * x + kx - 1) of the same image, and zero where that lies outside it.
+ */
+mxq_status mxq_conv3x3_gemm_mixed(const mxq_qtensor* x, int64_t height, int64_t width,
+                                  const mxq_qtensor* w_groups, int32_t n_groups,
+                                  const int32_t* w_perm, const void* bias, void* out,
+                                  int64_t ld_out, int64_t n_out, void* workspace,
+                                  size_t ws_bytes, void* stream);
+
+/*
  * mxq_select_format -- per-output-channel weight format by least
  * reconstruction error (Chameleon article, "the format is chosen by the
  * value distribution").

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(mxq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -93,6 +93,25 @@ def test_validation_before_device_work(lib):
     assert lib.mxq_gemm(C.byref(a), C.byref(w), None, None, 0, None, 0, None, vp(64), 8, 8, None, 0, None) == 2
     a2 = _lib.QTensorC(1, 0, 8, 256, vp(4096), 128, vp(8192), 8, None)
     assert lib.mxq_gemm(C.byref(a2), C.byref(w), None, None, 0, None, 0, None, vp(64), 8, 8, None, 0, None) == 4
+    # convolution: MXFP4 x MXFP4, C not a multiple of 128, pixels not whole
+    # images, weight K != 9 C, bad size, two groups without a permutation,
+    # empty input
+    x4 = _lib.QTensorC(1, 0, 40, 128, vp(4096), 64, vp(8192), 4, None)
+    w4 = _lib.QTensorC(1, 0, 8, 1152, vp(4096), 576, vp(8192), 36, None)
+    wn = _lib.QTensorC(3, 0, 8, 1152, vp(4096), 576, vp(8192), 72, vp(12288))
+    conv = lib.mxq_conv3x3_gemm_mixed
+    assert conv(C.byref(x4), 4, 5, C.byref(w4), 1, None, None, vp(64), 8, 8, None, 0, None) == 2
+    x64 = _lib.QTensorC(2, 0, 40, 64, vp(4096), 64, vp(8192), 4, None)
+    w64 = _lib.QTensorC(3, 0, 8, 576, vp(4096), 288, vp(8192), 36, vp(12288))
+    assert conv(C.byref(x64), 4, 5, C.byref(w64), 1, None, None, vp(64), 8, 8, None, 0, None) == 4
+    assert conv(C.byref(x4), 3, 5, C.byref(wn), 1, None, None, vp(64), 8, 8, None, 0, None) == 4
+    wbad = _lib.QTensorC(3, 0, 8, 1024, vp(4096), 512, vp(8192), 64, vp(12288))
+    assert conv(C.byref(x4), 4, 5, C.byref(wbad), 1, None, None, vp(64), 8, 8, None, 0, None) == 4
+    assert conv(C.byref(x4), 0, 5, C.byref(wn), 1, None, None, vp(64), 8, 8, None, 0, None) == 1
+    two = (_lib.QTensorC * 2)(wn, wn)
+    assert conv(C.byref(x4), 4, 5, two, 2, None, None, vp(64), 16, 16, None, 0, None) == 1
+    x0 = _lib.QTensorC(1, 0, 0, 128, None, 64, None, 4, None)
+    assert conv(C.byref(x0), 4, 5, C.byref(wn), 1, None, None, vp(64), 8, 8, None, 0, None) == 0
     # selection: unsupported candidate, bad K
     cand = (C.c_int32 * 1)(2)
     assert lib.mxq_select_format(vp(16), 1, 4, 64, 64, cand, 1, vp(64), None, None, None, None,
