@@ -109,6 +109,7 @@ def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None, conv="implici
     act = wl.activations(w)
     wt = wl.weights(w)
     fa, fw = wl_fmt(mxq, w.act_fmt), wl_fmt(mxq, w.w_fmt)
+    bf16_act = w.act_fmt == "BF16"   # unquantized activations: the GEMM reads x itself
     if w.act_dtype == "bf16":
         x0 = torch.from_numpy(act.view(np.int16)).view(torch.bfloat16).cuda()
     else:
@@ -123,8 +124,10 @@ def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None, conv="implici
     for i in range(n_sets):
         x = x0.clone()
         qw = mxq.quantize(w0, fw, hadamard=w.hadamard)
-        qa = mxq.empty_qtensor(fa, w.m, w.k)
-        ws = torch.empty((max(16, mxq.workspace_size(1, w.m, w.k, fa)),), dtype=torch.uint8, device="cuda")
+        qa = mxq.bf16_operand(x) if bf16_act else mxq.empty_qtensor(fa, w.m, w.k)
+        ws = torch.empty((max(16, mxq.workspace_size(mxq.OP_GEMM, w.m, w.n, fw),
+                              0 if bf16_act else mxq.workspace_size(mxq.OP_QUANTIZE, w.m, w.k, fa)),),
+                         dtype=torch.uint8, device="cuda")
         out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
         u = torch.empty((w.m, w.rank), dtype=torch.float32, device="cuda") if w.rank else None
         sets.append(dict(x=x, qw=qw, qa=qa, ws=ws, out=out, u=u,
@@ -136,7 +139,8 @@ def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None, conv="implici
 
 
 def wl_fmt(mxq, name: str) -> int:
-    return {"MXFP4": mxq.MXFP4, "MXFP8": mxq.MXFP8, "NVFP4": mxq.NVFP4, "INT4": mxq.INT4}[name]
+    return {"MXFP4": mxq.MXFP4, "MXFP8": mxq.MXFP8, "NVFP4": mxq.NVFP4, "INT4": mxq.INT4,
+            "BF16": mxq.BF16}[name]
 
 
 def set_bytes(s) -> int:
@@ -208,8 +212,8 @@ def cpu_baseline(w: wl.Workload, budget_s: float = 12.0) -> dict:
         pos += chunk.shape[0]
         t0 = time.perf_counter()
         r = oh.rotate(chunk, w.hadamard, 7) if w.hadamard else chunk
-        qa = oq.quantize(r, w.act_fmt)
-        y = og.linear(oq.dequantize(qa), w_deq)
+        a_deq = r if w.act_fmt == "BF16" else oq.dequantize(oq.quantize(r, w.act_fmt))
+        y = og.linear(a_deq, w_deq)
         if w.rank:
             y = y + og.lowrank_down(chunk, l1v) @ l2v
         round_to_bf16(y)
@@ -221,7 +225,8 @@ def cpu_baseline(w: wl.Workload, budget_s: float = 12.0) -> dict:
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{done_rows} rows ({done_rows / vals.shape[0]:.1f} passes over {vals.shape[0]} "
-                      f"of the {w.m} rows): oracle {w.act_fmt} quantize"
+                      f"of the {w.m} rows): oracle "
+                      f"{'bf16 activations' if w.act_fmt == 'BF16' else w.act_fmt + ' quantize'}"
                       f"{' + H' + str(w.hadamard) if w.hadamard else ''} + float64 GEMM "
                       f"against {w.w_fmt} weights{' + rank-' + str(w.rank) + ' branch' if w.rank else ''}"
                       f", {elapsed:.1f} s"}
@@ -262,7 +267,11 @@ def main() -> int:
         lat_h, lat_w, lat_c = w.extra["latent"]
     fa = wl_fmt(mxq, w.act_fmt)
 
+    bf16_act = w.act_fmt == "BF16"
+
     def quant(s):
+        if bf16_act:
+            return
         if mixed:
             mxq.quantize(s["x"], fa, out=s["qa"])
         else:
@@ -277,7 +286,7 @@ def main() -> int:
             mxq.gemm_mixed(s["qa"], s["groups"], s["perm"], w.n, out=s["out"],
                            workspace=s["ws"])
         else:
-            mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"])
+            mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"], workspace=s["ws"])
 
     def step(s):
         quant(s)
@@ -295,7 +304,8 @@ def main() -> int:
     # per-kernel durations: each kernel's launches over all buffer sets are
     # captured in a HIP graph and replayed between two HIP events on the
     # replay stream, so host launch gaps do not count
-    q_ms = graph_avg_ms(torch, [lambda s=s: quant(s) for s in sets], args.steps)
+    q_ms = None if bf16_act else graph_avg_ms(torch, [lambda s=s: quant(s) for s in sets],
+                                              args.steps)
     g_ms = graph_avg_ms(torch, [lambda s=s: gemm(s) for s in sets], args.steps)
     if args.copy_probe:
         a = torch.empty((1 << 28,), dtype=torch.float32, device="cuda")
@@ -316,7 +326,7 @@ def main() -> int:
         ent = t.get(w.name)
         if ent and ent.get("kernel_source_digest") == kernel_source_digest():
             traffic = ent.get("gemm_hbm_bytes_per_launch")
-    qbytes = quantize_bytes(w, lat_c if implicit else None)
+    qbytes = None if bf16_act else quantize_bytes(w, lat_c if implicit else None)
     rec = {
         "metric": "block-scaled GEMM TFLOP/s & % MXFP4 peak; quantize GB/s & % HBM BW",
         "value": round(2.0 * w.m * w.n * w.k / (ms * 1e-3) / 1e12, 2),
@@ -339,9 +349,10 @@ def main() -> int:
                      "frac": round(achieved / PEAK_TFLOPS[gdt], 4), "traffic": traffic,
                      "kernel": "gemm", "avg_launch_us": round(g_ms * 1e3, 3)},
         "gemm_pct_mxfp4_peak": round(achieved / PEAK_TFLOPS["mxfp4"], 4),
-        "quantize": {"avg_launch_us": round(q_ms * 1e3, 3), "algorithmic_bytes": qbytes,
-                     "GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
-                     "frac_hbm": round(qbytes / (q_ms * 1e-3) / 1e9 / HBM_GBPS, 4)},
+        "quantize": None if bf16_act else {
+            "avg_launch_us": round(q_ms * 1e3, 3), "algorithmic_bytes": qbytes,
+            "GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
+            "frac_hbm": round(qbytes / (q_ms * 1e-3) / 1e9 / HBM_GBPS, 4)},
         "kernel_source_digest": kernel_source_digest(),
     }
     if mixed:

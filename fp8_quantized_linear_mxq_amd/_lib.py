@@ -14,6 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmxq.so")
 
 MXFP4, MXFP8, NVFP4, INT4 = 1, 2, 3, 4
+BF16 = 5   # unquantized bf16 activations (GEMM operand only)
 FORMATS = {"MXFP4": MXFP4, "MXFP8": MXFP8, "NVFP4": NVFP4, "INT4": INT4}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 DT_F32, DT_BF16 = 1, 2
@@ -155,6 +156,15 @@ def empty_qtensor(fmt: int, rows: int, cols: int, device="cuda") -> QTensor:
         scales = torch.empty((rows, (sb + 3) // 4 * 4), dtype=torch.uint8, device=device)
     ts = torch.empty((1,), dtype=torch.float32, device=device) if fmt == NVFP4 else None
     return QTensor(fmt, rows, cols, codes, scales, ts)
+
+
+def bf16_operand(x) -> QTensor:
+    """A 2-D cuda bfloat16 tensor as the GEMM's unquantized activation
+    operand (4-bit weights, 16-bit activations)."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("bf16_operand needs a row-major 2-D bfloat16 tensor")
+    return QTensor(BF16, x.shape[0], x.shape[1], x, None)
 
 
 def quantize(x, fmt: int, hadamard: int = 0, static_tensor_scale=None, l1t=None, u=None,

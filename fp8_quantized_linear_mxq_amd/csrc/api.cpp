@@ -19,11 +19,15 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 int block_of(int fmt) { return fmt == MXQ_FMT_NVFP4 ? 16 : 32; }
 
+// The quantized formats (BF16, unquantized activations, is separate).
 bool known_fmt(int fmt) { return fmt >= MXQ_FMT_MXFP4 && fmt <= MXQ_FMT_INT4; }
 
-int64_t code_bytes(int fmt, int64_t cols) { return fmt == MXQ_FMT_MXFP8 ? cols : cols / 2; }
+int64_t code_bytes(int fmt, int64_t cols) {
+  return fmt == MXQ_FMT_BF16 ? 2 * cols : fmt == MXQ_FMT_MXFP8 ? cols : cols / 2;
+}
 
 int64_t scale_bytes(int fmt, int64_t cols) {
+  if (fmt == MXQ_FMT_BF16) return 0;
   const int64_t blocks = cols / block_of(fmt);
   return fmt == MXQ_FMT_INT4 ? blocks * 4 : blocks;
 }
@@ -32,6 +36,14 @@ mxq_status from_hip(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_LA
 
 // Validates a quantized operand's descriptor against its format.
 mxq_status check_qtensor(const mxq_qtensor* t) {
+  if (t && t->fmt == MXQ_FMT_BF16) {
+    // unquantized bf16 values in `codes`; no scales
+    if (t->reserved != 0 || t->rows < 0 || t->cols < 0) return MXQ_ERR_INVALID_ARG;
+    if (t->rows == 0 || t->cols == 0) return MXQ_OK;
+    if (!t->codes || t->ld_codes < 2 * t->cols) return MXQ_ERR_INVALID_ARG;
+    if (!aligned(t->codes, 16) || t->ld_codes % 16) return MXQ_ERR_ALIGNMENT;
+    return MXQ_OK;
+  }
   if (!t || !known_fmt(t->fmt) || t->reserved != 0 || t->rows < 0 || t->cols < 0)
     return MXQ_ERR_INVALID_ARG;
   if (t->cols % block_of(t->fmt)) return MXQ_ERR_SHAPE;
@@ -173,8 +185,9 @@ static mxq_status gemm_checks(const mxq_qtensor* a, const mxq_qtensor* w, const 
   if (st != MXQ_OK) return st;
   if (a->cols != w->cols) return MXQ_ERR_SHAPE;
   if (n_out < 0 || lr_rank < 0 || lr_rank > 128 || lr_rank % 16) return MXQ_ERR_INVALID_ARG;
-  // activations: MXFP4, MXFP8 or NVFP4; weights: MXFP4, NVFP4 or INT4
-  if (a->fmt == MXQ_FMT_INT4 || w->fmt == MXQ_FMT_MXFP8) return MXQ_ERR_UNSUPPORTED;
+  // activations: MXFP4, MXFP8, NVFP4 or bf16; weights: MXFP4, NVFP4 or INT4
+  if (a->fmt == MXQ_FMT_INT4 || w->fmt == MXQ_FMT_MXFP8 || w->fmt == MXQ_FMT_BF16)
+    return MXQ_ERR_UNSUPPORTED;
   if (a->rows == 0 || w->rows == 0 || n_out == 0) return MXQ_OK;
   if (a->cols % 128) return MXQ_ERR_SHAPE;
   if (a->rows > INT32_MAX || w->rows > INT32_MAX || a->cols > INT32_MAX || n_out > INT32_MAX)
@@ -284,7 +297,7 @@ mxq_status mxq_conv3x3_gemm_mixed(const mxq_qtensor* x, int64_t height, int64_t 
   mxq_status st = check_qtensor(x);
   if (st != MXQ_OK) return st;
   if (height <= 0 || width <= 0 || n_out < 0) return MXQ_ERR_INVALID_ARG;
-  if (x->fmt == MXQ_FMT_INT4) return MXQ_ERR_UNSUPPORTED;
+  if (x->fmt == MXQ_FMT_INT4 || x->fmt == MXQ_FMT_BF16) return MXQ_ERR_UNSUPPORTED;
   if (workspace && !aligned(workspace, 16)) return MXQ_ERR_ALIGNMENT;
   if (height > INT32_MAX / width) return MXQ_ERR_SHAPE;
   const int64_t C = x->cols, hw = height * width;
@@ -296,7 +309,7 @@ mxq_status mxq_conv3x3_gemm_mixed(const mxq_qtensor* x, int64_t height, int64_t 
     const mxq_qtensor* w = &w_groups[g];
     st = check_qtensor(w);
     if (st != MXQ_OK) return st;
-    if (w->fmt == MXQ_FMT_MXFP8) return MXQ_ERR_UNSUPPORTED;
+    if (w->fmt == MXQ_FMT_MXFP8 || w->fmt == MXQ_FMT_BF16) return MXQ_ERR_UNSUPPORTED;
     // the scaled-MFMA route (MXFP4 x MXFP4) reads no implicit im2col
     if (x->fmt == MXQ_FMT_MXFP4 && w->fmt == MXQ_FMT_MXFP4 && w->rows > 0)
       return MXQ_ERR_UNSUPPORTED;

@@ -13,7 +13,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // Format identifiers (same values as mxq_format in mxq.h).
-enum : int { FMT_MXFP4 = 1, FMT_MXFP8 = 2, FMT_NVFP4 = 3, FMT_INT4 = 4 };
+enum : int { FMT_MXFP4 = 1, FMT_MXFP8 = 2, FMT_NVFP4 = 3, FMT_INT4 = 4, FMT_BF16 = 5 };
 enum : int { DT_F32 = 1, DT_BF16 = 2 };
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {

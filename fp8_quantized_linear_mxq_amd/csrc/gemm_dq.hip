@@ -1,5 +1,6 @@
 // GEMM route for INT4 weight rows (Chameleon palette: symmetric int4 with an
-// fp32 scale per 32), against MXFP8, NVFP4 or MXFP4 activations.
+// fp32 scale per 32), against MXFP8, NVFP4 or MXFP4 activations, or
+// unquantized bf16 activations (4-bit weights, 16-bit activations).
 //
 // The arbitrary fp32 weight scale cannot fold into a 16-bit operand, so each
 // 32-element block's partial sum comes from two bf16 MFMAs on the integer
@@ -29,7 +30,7 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-enum : int { K_NV = 0, K_MX8 = 1, K_MX4 = 2, K_I4 = 3 };
+enum : int { K_NV = 0, K_MX8 = 1, K_MX4 = 2, K_I4 = 3, K_BF = 4 };
 
 struct DqParams {
   GemmP g;
@@ -191,8 +192,24 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
   const int fr = tid >> 1, fc = tid & 1;      // 4-bit operands: row, 32-element chunk
   Fp4Loader<WK> wl;
   wl.init(p.w, p.ldw, p.ws, p.ldws, n0 + fr, p.N, fc);
-  Fp4Loader<AK == K_MX8 ? K_MX4 : AK> al;     // unused for E4M3 activations
-  if constexpr (AK != K_MX8) al.init(p.a, p.lda, p.as, p.ldas, m0 + fr, p.M, fc);
+  Fp4Loader<(AK == K_MX8 || AK == K_BF) ? K_MX4 : AK> al;   // 4-bit activations only
+  if constexpr (AK != K_MX8 && AK != K_BF) al.init(p.a, p.lda, p.as, p.ldas, m0 + fr, p.M, fc);
+  // bf16 activations: four 16-byte chunks (8 elements each) per thread,
+  // copied to LDS unchanged.
+  int rbf[4], cbf[4];
+  const uint8_t* a_bf[4];
+  bool a_okbf[4];
+  uint4 rabf[4];
+  if constexpr (AK == K_BF) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + i * kThreads;
+      rbf[i] = q >> 3;
+      cbf[i] = q & 7;
+      a_okbf[i] = (m0 + rbf[i]) < p.M;
+      a_bf[i] = p.a + (int64_t)(a_okbf[i] ? m0 + rbf[i] : 0) * p.lda + cbf[i] * 16;
+    }
+  }
   // E4M3 activations: two 16-byte chunks (16 elements each) per thread.
   int ar8[2], ac8[2];
   bool a_ok8[2];
@@ -257,6 +274,11 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
                           : make_uint4(0, 0, 0, 0);
         ras8[i] = a_scl8[i][kt * 2 + (ac8[i] >> 1)];
       }
+    } else if constexpr (AK == K_BF) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rabf[i] = a_okbf[i] ? *reinterpret_cast<const uint4*>(a_bf[i] + (int64_t)kt * 128)
+                            : make_uint4(0, 0, 0, 0);
     } else {
       al.load(kt);
     }
@@ -273,7 +295,11 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
       const int c = fc * 4 + k;
       *reinterpret_cast<uint4*>(&sB[buf][fr * RB + ((c ^ swz<CH>(fr)) * 16)]) = o[k];
     }
-    if constexpr (AK == K_MX8) {
+    if constexpr (AK == K_BF) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(&sA[buf][rbf[i] * RB + ((cbf[i] ^ swz<CH>(rbf[i])) * 16)]) = rabf[i];
+    } else if constexpr (AK == K_MX8) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         uint4 o2[2];
@@ -417,9 +443,15 @@ __global__ __launch_bounds__(kThreads) void conv_dq_kernel(DqParams dp) {
 
 template <int AK, int WK>
 hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
-  if (p.g.cv_c > 0) conv_dq_kernel<AK, WK><<<grid, kThreads, 0, s>>>(p);
-  else if (lr) gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
-  else gemm_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
+  if (p.g.cv_c > 0) {
+    // implicit im2col of a quantized input (none for bf16 input)
+    if constexpr (AK == K_BF) return hipErrorInvalidValue;
+    else conv_dq_kernel<AK, WK><<<grid, kThreads, 0, s>>>(p);
+  } else if (lr) {
+    gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
+  } else {
+    gemm_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.part) return e;
   return launch_splitk_reduce(p.g, p.part, (int)grid.y, AK == K_NV ? p.a_gp : nullptr, s);
@@ -477,6 +509,7 @@ hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s) {
     case FMT_NVFP4: return dispatch_w<K_NV>(a.w_fmt, lr, grid, dp, s);
     case FMT_MXFP8: return dispatch_w<K_MX8>(a.w_fmt, lr, grid, dp, s);
     case FMT_MXFP4: return dispatch_w<K_MX4>(a.w_fmt, lr, grid, dp, s);
+    case FMT_BF16: return dispatch_w<K_BF>(a.w_fmt, lr, grid, dp, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,6 +1,8 @@
 // Pipelined exact-dequant GEMM for MX/NVFP4 weights: every (activation,
 // weight) pair with A in {MXFP8, NVFP4, MXFP4} and W in {MXFP4, NVFP4} except
-// MXFP4 x MXFP4, which has its own scaled-MFMA kernel.
+// MXFP4 x MXFP4, which has its own scaled-MFMA kernel; also unquantized bf16
+// activations (4-bit weights, 16-bit activations), which skip the activation
+// dequantization.
 //
 // Arithmetic (why 16-bit): on gfx950 the MFMAs that take E4M3 operands keep
 // only about 15 bits below the largest product of each dot product, which
@@ -40,13 +42,13 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-enum : int { K_NV = 0, K_MX8 = 1, K_MX4 = 2 };
+enum : int { K_NV = 0, K_MX8 = 1, K_MX4 = 2, K_BF = 3 };
 
 constexpr int BK = 128;
 constexpr int kSlab = 6;   // K-tiles (8 MFMA steps each) per fp32 slab when slabbing
 
-template <int K> constexpr int row_bytes() { return K == K_MX8 ? 128 : 64; }
-template <int K> constexpr int scale_bytes() { return K == K_NV ? 8 : 4; }
+template <int K> constexpr int row_bytes() { return K == K_BF ? 256 : K == K_MX8 ? 128 : 64; }
+template <int K> constexpr int scale_bytes() { return K == K_BF ? 0 : K == K_NV ? 8 : 4; }
 
 struct DqpParams {
   GemmP g;
@@ -75,7 +77,9 @@ struct Scales {
 template <int K, bool FP16>
 __device__ __forceinline__ Scales<K, FP16> lane_scales(uint32_t dw, int half) {
   Scales<K, FP16> r;
-  if constexpr (K == K_NV) {
+  if constexpr (K == K_BF) {
+    r.s[0] = r.s[1] = 1.0f;   // no scales
+  } else if constexpr (K == K_NV) {
     // dword `half` of the row's 8 scale bytes: 16-blocks 4h .. 4h+3
 #pragma unroll
     for (int q = 0; q < 4; ++q) r.s[q] = e4m3_value((dw >> (8 * q)) & 0xFFu);
@@ -91,7 +95,9 @@ __device__ __forceinline__ Scales<K, FP16> lane_scales(uint32_t dw, int half) {
 // Dequantize MFMA step ks (8 elements) of a lane's raw run to 16-bit values.
 template <int K, bool FP16>
 __device__ __forceinline__ uint4 dq(const uint32_t* raw, int ks, const Scales<K, FP16>& sc) {
-  if constexpr (K == K_MX8) {
+  if constexpr (K == K_BF) {
+    return make_uint4(raw[4 * ks], raw[4 * ks + 1], raw[4 * ks + 2], raw[4 * ks + 3]);
+  } else if constexpr (K == K_MX8) {
     const float s = sc.s[ks >> 2];
     const uint32_t d0 = raw[2 * ks], d1 = raw[2 * ks + 1];
     return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d0, s, false)),
@@ -292,7 +298,8 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
     Scales<WK, FP16> sw[TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
-      sa[i] = lane_scales<AK, FP16>(*reinterpret_cast<const uint32_t*>(st + sa_base + i * 32 * SBA), half);
+      sa[i] = SBA ? lane_scales<AK, FP16>(*reinterpret_cast<const uint32_t*>(st + sa_base + i * 32 * SBA), half)
+                  : lane_scales<AK, FP16>(0u, half);
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       sw[j] = lane_scales<WK, FP16>(*reinterpret_cast<const uint32_t*>(st + sw_base + j * 32 * SBW), half);
@@ -434,8 +441,7 @@ hipError_t launch_conv(DqpParams dp, hipStream_t s) {
 }
 
 template <int AK, int WK>
-hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
-  if (dp.g.cv_c > 0) return launch_conv<AK, WK>(dp, s);
+hipError_t launch_tiles(bool lr, const DqpParams& dp, hipStream_t s) {
   const int64_t M = dp.g.M, N = dp.g.N;
   // past 32 K-tiles the fp32 chains are flushed into a second accumulator
   // every kSlab K-tiles, which only the small tile has the registers for
@@ -466,6 +472,20 @@ hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
   return launch_cfg<AK, WK, 4, 2, false>(lr, dp, s);
 }
 
+template <int AK, int WK>
+hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
+  if constexpr (AK == K_BF) {
+    // 16-bit activation tiles are 256 bytes a row: only the 128x128 tile's
+    // three stages (123 KB) fit in LDS
+    if (dp.g.cv_c > 0) return hipErrorInvalidValue;
+    if (dp.g.K / BK > 32) return launch_cfg<AK, WK, 2, 2, true>(lr, dp, s);
+    return launch_cfg<AK, WK, 2, 2, false>(lr, dp, s);
+  } else {
+    if (dp.g.cv_c > 0) return launch_conv<AK, WK>(dp, s);
+    return launch_tiles<AK, WK>(lr, dp, s);
+  }
+}
+
 template <int AK>
 hipError_t launch_w(int w_fmt, bool lr, const DqpParams& dp, hipStream_t s) {
   if (w_fmt == FMT_NVFP4) return launch_pair<AK, K_NV>(lr, dp, s);
@@ -494,6 +514,7 @@ hipError_t launch_gemm_dqp(const GemmArgs& a, hipStream_t s) {
     case FMT_NVFP4: return launch_w<K_NV>(a.w_fmt, lr, dp, s);
     case FMT_MXFP8: return launch_w<K_MX8>(a.w_fmt, lr, dp, s);
     case FMT_MXFP4: return launch_w<K_MX4>(a.w_fmt, lr, dp, s);
+    case FMT_BF16: return launch_w<K_BF>(a.w_fmt, lr, dp, s);
     default: return hipErrorInvalidValue;
   }
 }

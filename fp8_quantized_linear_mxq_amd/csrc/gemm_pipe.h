@@ -77,6 +77,7 @@ __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0,
                                                  int lim_w = SBW / 4) {
   constexpr int DA = TBM * SBA / 4, D = DA + TBN * SBW / 4;
   constexpr int PERW = (D + 64 * NW - 1) / (64 * NW);
+  constexpr int QA = SBA >= 4 ? SBA / 4 : 1;   // dwords per A row (A may have no scales)
 #pragma unroll
   for (int t = 0; t < PERW; ++t) {
     const int slot0 = (t * NW + wave) * 64;
@@ -84,10 +85,10 @@ __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0,
     const uint8_t* src;
     bool cut = false;
     if (d < DA) {
-      int r = m0 + d / (SBA / 4);
+      int r = m0 + d / QA;
       r = r < p.M ? r : p.M - 1;
-      cut = lim_a < SBA / 4 && d % (SBA / 4) >= lim_a;
-      src = p.as + (int64_t)r * p.ldas + kt * SBA + (d % (SBA / 4)) * 4;
+      cut = lim_a < SBA / 4 && d % QA >= lim_a;
+      src = p.as + (int64_t)r * p.ldas + kt * SBA + (d % QA) * 4;
     } else if (d < D) {
       const int e = d - DA;
       int r = n0 + e / (SBW / 4);
@@ -95,7 +96,7 @@ __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0,
       cut = lim_w < SBW / 4 && e % (SBW / 4) >= lim_w;
       src = p.ws + (int64_t)r * p.ldws + kt * SBW + (e % (SBW / 4)) * 4;
     } else {
-      src = p.as + (int64_t)(m0 < p.M ? m0 : p.M - 1) * p.ldas + kt * SBA;
+      src = SBA ? p.as + (int64_t)(m0 < p.M ? m0 : p.M - 1) * p.ldas + kt * SBA : g_zero16;
     }
     src = (zero || cut) ? g_zero16 : src;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + slot0 * 4), 4, 0, 0);

@@ -86,7 +86,14 @@ typedef enum mxq_format {
   MXQ_FMT_MXFP4 = 1,
   MXQ_FMT_MXFP8 = 2,
   MXQ_FMT_NVFP4 = 3,
-  MXQ_FMT_INT4 = 4
+  MXQ_FMT_INT4 = 4,
+  /* Unquantized bf16 activations (4-bit weights, 16-bit activations; the
+   * Nunchaku article, "kernels and supported hardware": the second kernel
+   * type, for the adaptive-normalization layers that need the precision).
+   * Only as mxq_gemm / mxq_gemm_mixed's `a`: codes holds the bf16 values
+   * [rows][ld_codes bytes] (16-byte aligned, ld_codes a multiple of 16),
+   * scales and tensor_scale are unused.  Not a quantize target. */
+  MXQ_FMT_BF16 = 5
 } mxq_format;
 
 typedef enum mxq_dtype { MXQ_DT_F32 = 1, MXQ_DT_BF16 = 2 } mxq_dtype;
@@ -148,7 +155,8 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
  * format (Nunchaku article, main explanation: 4-bit GEMM plus the 16-bit
  * low-rank branch added in the same output).
  *
- *  a           quantized activations [M, K]: MXFP4, MXFP8 or NVFP4.
+ *  a           quantized activations [M, K]: MXFP4, MXFP8 or NVFP4; or
+ *              unquantized bf16 activations (MXQ_FMT_BF16), taken exactly.
  *  w           quantized weights [N, K]: MXFP4, NVFP4 or INT4.  Every pair
  *              is supported: MXFP4 x MXFP4 on the scaled MFMA; the others
  *              dequantize exactly to fp16 (NVFP4 x NVFP4) or bf16 operands;
@@ -208,7 +216,7 @@ mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int
  *
  *  x           quantized input [images * height * width][C] (pixel rows in
  *              row-major image, y, x order; C channels): MXFP8, NVFP4 or
- *              MXFP4.  C must be a multiple of 128.
+ *              MXFP4 (not bf16).  C must be a multiple of 128.
  *  height, width  the spatial size of each image (> 0); x->rows must be a
  *              multiple of height * width.
  *  w_groups, n_groups, w_perm  weight groups as in mxq_gemm_mixed, each

@@ -112,6 +112,15 @@ def test_validation_before_device_work(lib):
     assert conv(C.byref(x4), 4, 5, two, 2, None, None, vp(64), 16, 16, None, 0, None) == 1
     x0 = _lib.QTensorC(1, 0, 0, 128, None, 64, None, 4, None)
     assert conv(C.byref(x0), 4, 5, C.byref(wn), 1, None, None, vp(64), 8, 8, None, 0, None) == 0
+    # bf16 activations: not a weight format, not a quantize target, rows
+    # misaligned; an empty bf16 operand is a no-op
+    ab = _lib.QTensorC(5, 0, 8, 128, vp(4096), 256, None, 0, None)
+    assert lib.mxq_gemm(C.byref(w), C.byref(ab), None, None, 0, None, 0, None, vp(64), 8, 8, None, 0, None) == 2
+    assert lib.mxq_quantize(vp(16), 1, 8, 128, 128, 0, None, None, 0, None, 0, C.byref(ab), None, 0, None) == 1
+    abm = _lib.QTensorC(5, 0, 8, 128, vp(4096), 264, None, 0, None)
+    assert lib.mxq_gemm(C.byref(abm), C.byref(w), None, None, 0, None, 0, None, vp(64), 8, 8, None, 0, None) == 3
+    ab0 = _lib.QTensorC(5, 0, 0, 128, None, 256, None, 0, None)
+    assert lib.mxq_gemm(C.byref(ab0), C.byref(w), None, None, 0, None, 0, None, vp(64), 8, 8, None, 0, None) == 0
     # selection: unsupported candidate, bad K
     cand = (C.c_int32 * 1)(2)
     assert lib.mxq_select_format(vp(16), 1, 4, 64, 64, cand, 1, vp(64), None, None, None, None,
