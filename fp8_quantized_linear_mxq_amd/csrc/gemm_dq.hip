@@ -127,6 +127,12 @@ __device__ __forceinline__ float e8m0_f32(uint32_t code) {
   return code == 0 ? 0x1p-127f : __uint_as_float(code << 23);
 }
 
+// A thread's staged 4-bit chunk of one K-tile: 32 codes and their scales.
+struct Fp4Data {
+  uint4 r;
+  uint32_t s;
+};
+
 // Loader of one 4-bit operand (A or W): a 16-byte chunk of 32 codes per
 // thread per K-tile, plus its block scales.
 template <int KIND>
@@ -135,8 +141,6 @@ struct Fp4Loader {
   const uint8_t* scl;
   bool ok;
   int fc;
-  uint4 r;
-  uint32_t s;
   __device__ void init(const uint8_t* base, int64_t ld, const uint8_t* sbase, int64_t lds, int row,
                        int nrows, int fc_) {
     fc = fc_;
@@ -144,35 +148,37 @@ struct Fp4Loader {
     code = base + (int64_t)(ok ? row : 0) * ld + fc * 16;
     scl = sbase + (int64_t)(ok ? row : 0) * lds;
   }
-  __device__ void load(int kt) {
-    r = ok ? *reinterpret_cast<const uint4*>(code + (int64_t)kt * 32) : make_uint4(0, 0, 0, 0);
-    if constexpr (KIND == K_NV) s = *reinterpret_cast<const uint32_t*>(scl + kt * 4);  // 4 x E4M3
-    else if constexpr (KIND == K_MX4) s = scl[kt * 2 + fc];                            // E8M0
+  __device__ void load(int kt, Fp4Data& d) const {
+    d.r = ok ? *reinterpret_cast<const uint4*>(code + (int64_t)kt * 32) : make_uint4(0, 0, 0, 0);
+    if constexpr (KIND == K_NV) d.s = *reinterpret_cast<const uint32_t*>(scl + kt * 4);  // 4 x E4M3
+    else if constexpr (KIND == K_MX4) d.s = scl[kt * 2 + fc];                            // E8M0
   }
   // Implicit im2col: K-tile kc of the channel row of the pixel `shift` rows
   // away, or zero codes and scales when that pixel is outside the image.
-  __device__ void load_conv(int kc, int64_t shift, int64_t ld, int64_t lds, bool in) {
-    r = (ok && in) ? *reinterpret_cast<const uint4*>(code + shift * ld + (int64_t)kc * 32)
-                   : make_uint4(0, 0, 0, 0);
+  __device__ void load_conv(int kc, int64_t shift, int64_t ld, int64_t lds, bool in,
+                            Fp4Data& d) const {
+    d.r = (ok && in) ? *reinterpret_cast<const uint4*>(code + shift * ld + (int64_t)kc * 32)
+                     : make_uint4(0, 0, 0, 0);
     const uint8_t* sp = in ? scl + shift * lds : scl;
     uint32_t v = 0;
     if constexpr (KIND == K_NV) v = *reinterpret_cast<const uint32_t*>(sp + kc * 4);
     else if constexpr (KIND == K_MX4) v = sp[kc * 2 + fc];
-    s = in ? v : 0u;
+    d.s = in ? v : 0u;
   }
   template <bool FP16>
-  __device__ void convert(uint4 o[4]) const {
+  __device__ void convert(const Fp4Data& d, uint4 o[4]) const {
     if constexpr (KIND == K_NV) {
-      dq_fp4_nv<FP16>(r, e4m3_value((s >> (16 * fc)) & 0xFFu), e4m3_value((s >> (16 * fc + 8)) & 0xFFu), o);
+      dq_fp4_nv<FP16>(d.r, e4m3_value((d.s >> (16 * fc)) & 0xFFu),
+                      e4m3_value((d.s >> (16 * fc + 8)) & 0xFFu), o);
     } else if constexpr (KIND == K_MX4) {
-      dq_fp4_mx(r, e8m0_f32(s), o);
+      dq_fp4_mx(d.r, e8m0_f32(d.s), o);
     } else {
-      dq_int4(r, o);
+      dq_int4(d.r, o);
     }
   }
 };
 
-template <int AK, int WK, bool LR, bool CONV>
+template <int AK, int WK, bool LR, bool CONV, bool DEEP>
 __device__ __forceinline__ void dq_body(const DqParams& dp) {
   const GemmP& p = dp.g;
   constexpr bool FP16 = (AK == K_NV && WK == K_NV);
@@ -199,7 +205,6 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
   int rbf[4], cbf[4];
   const uint8_t* a_bf[4];
   bool a_okbf[4];
-  uint4 rabf[4];
   if constexpr (AK == K_BF) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -215,8 +220,6 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
   bool a_ok8[2];
   const uint8_t* a_code8[2];
   const uint8_t* a_scl8[2];
-  uint4 ra8[2];
-  uint32_t ras8[2];
   if constexpr (AK == K_MX8) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -239,7 +242,7 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
   }
   // INT4 weights: this lane's output columns' fp32 block scales.
   const float* sw_row[2];
-  float2 sw[2], nsw[2];
+  float2 sw[2];
   if constexpr (I4) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -248,48 +251,57 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
     }
   }
 
-  auto gload = [&](int kt) {
-    wl.load(kt);
+  // One K-tile's global loads, held in registers until stored to LDS (two
+  // tiles are in flight: each has a full K-tile of compute to land).
+  struct Stage {
+    Fp4Data w;        // weight codes and scales
+    Fp4Data a;        // 4-bit activations
+    uint4 a16[4];     // bf16 activations (4 chunks) or E4M3 (2 chunks)
+    uint32_t a8s[2];  // E4M3 activations' E8M0 scales
+    float2 sc[2];     // INT4 weights' block scales of this lane's columns
+  };
+  auto gload = [&](int kt, Stage& S) __attribute__((always_inline)) {
+    wl.load(kt, S.w);
     if constexpr (CONV) {
       const ConvTap tp = conv_tap(p, kt, BK);
       if constexpr (AK == K_MX8) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const bool in = conv_inside(p, tp, cv_y[i], cv_x[i]);
-          ra8[i] = (a_ok8[i] && in)
-                       ? *reinterpret_cast<const uint4*>(a_code8[i] + (int64_t)tp.shift * p.lda +
-                                                         (int64_t)tp.kc * 64)
-                       : make_uint4(0, 0, 0, 0);
+          S.a16[i] = (a_ok8[i] && in)
+                         ? *reinterpret_cast<const uint4*>(a_code8[i] + (int64_t)tp.shift * p.lda +
+                                                           (int64_t)tp.kc * 64)
+                         : make_uint4(0, 0, 0, 0);
           const uint8_t* sp = in ? a_scl8[i] + (int64_t)tp.shift * p.ldas : a_scl8[i];
           const uint32_t v = sp[tp.kc * 2 + (ac8[i] >> 1)];
-          ras8[i] = in ? v : 0u;
+          S.a8s[i] = in ? v : 0u;
         }
       } else {
-        al.load_conv(tp.kc, tp.shift, p.lda, p.ldas, conv_inside(p, tp, cv_y[0], cv_x[0]));
+        al.load_conv(tp.kc, tp.shift, p.lda, p.ldas, conv_inside(p, tp, cv_y[0], cv_x[0]), S.a);
       }
     } else if constexpr (AK == K_MX8) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        ra8[i] = a_ok8[i] ? *reinterpret_cast<const uint4*>(a_code8[i] + (int64_t)kt * 64)
-                          : make_uint4(0, 0, 0, 0);
-        ras8[i] = a_scl8[i][kt * 2 + (ac8[i] >> 1)];
+        S.a16[i] = a_ok8[i] ? *reinterpret_cast<const uint4*>(a_code8[i] + (int64_t)kt * 64)
+                            : make_uint4(0, 0, 0, 0);
+        S.a8s[i] = a_scl8[i][kt * 2 + (ac8[i] >> 1)];
       }
     } else if constexpr (AK == K_BF) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        rabf[i] = a_okbf[i] ? *reinterpret_cast<const uint4*>(a_bf[i] + (int64_t)kt * 128)
-                            : make_uint4(0, 0, 0, 0);
+        S.a16[i] = a_okbf[i] ? *reinterpret_cast<const uint4*>(a_bf[i] + (int64_t)kt * 128)
+                             : make_uint4(0, 0, 0, 0);
     } else {
-      al.load(kt);
+      al.load(kt, S.a);
     }
     if constexpr (I4) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) nsw[j] = *reinterpret_cast<const float2*>(sw_row[j] + kt * 2);
+      for (int j = 0; j < 2; ++j) S.sc[j] = *reinterpret_cast<const float2*>(sw_row[j] + kt * 2);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const Stage& S) __attribute__((always_inline)) {
     uint4 o[4];
-    wl.template convert<FP16>(o);
+    wl.template convert<FP16>(S.w, o);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int c = fc * 4 + k;
@@ -298,12 +310,12 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
     if constexpr (AK == K_BF) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4*>(&sA[buf][rbf[i] * RB + ((cbf[i] ^ swz<CH>(rbf[i])) * 16)]) = rabf[i];
+        *reinterpret_cast<uint4*>(&sA[buf][rbf[i] * RB + ((cbf[i] ^ swz<CH>(rbf[i])) * 16)]) = S.a16[i];
     } else if constexpr (AK == K_MX8) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         uint4 o2[2];
-        dq_fp8_mx(ra8[i], e8m0_f32(ras8[i]), o2);
+        dq_fp8_mx(S.a16[i], e8m0_f32(S.a8s[i]), o2);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int c = ac8[i] * 2 + k;
@@ -311,7 +323,7 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
         }
       }
     } else {
-      al.template convert<FP16>(o);
+      al.template convert<FP16>(S.a, o);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int c = fc * 4 + k;
@@ -339,16 +351,9 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
       tot[i][j] = v16f{};
     }
 
-  gload(kt0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = kt0; kt < KT; ++kt) {
+  // Multiply K-tile kt from LDS buffer (kt - kt0) & 1 (INT4 block scales in sw).
+  auto mma = [&](int kt) __attribute__((always_inline)) {
     const int buf = (kt - kt0) & 1;
-    if constexpr (I4) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) sw[j] = nsw[j];
-    }
-    if (kt + 1 < KT) gload(kt + 1);
     uint4 af[BK / 16][2], bf[BK / 16][2];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks)
@@ -398,8 +403,49 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
           acc[i][j] = v16f{};
         }
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
+  };
+
+  if constexpr (DEEP) {
+    // Two K-tiles in flight.  At K-tile kt the stage `mine` is free (its
+    // INT4 scales are copied first) and `nxt` holds K-tile kt + 1: load
+    // K-tile kt + 2 into `mine`, multiply K-tile kt, store K-tile kt + 1.
+    // The load is unconditional (the last ones reload K-tile KT - 1): one
+    // under a branch would make the compiler wait for it before the store.
+    auto iter = [&](int kt, Stage& mine, Stage& nxt) __attribute__((always_inline)) {
+      if constexpr (I4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sw[j] = mine.sc[j];
+      }
+      gload(kt + 2 < KT ? kt + 2 : KT - 1, mine);
+      mma(kt);
+      if (kt + 1 < KT) lstore(((kt - kt0) & 1) ^ 1, nxt);
+      __syncthreads();
+    };
+    Stage sg0, sg1;
+    gload(kt0, sg0);
+    gload(kt0 + 1 < KT ? kt0 + 1 : KT - 1, sg1);
+    lstore(0, sg0);
     __syncthreads();
+    for (int kt = kt0; kt < KT; kt += 2) {
+      iter(kt, sg0, sg1);
+      if (kt + 1 < KT) iter(kt + 1, sg1, sg0);
+    }
+  } else {
+    // One K-tile in flight: load K-tile kt + 1, multiply K-tile kt, store.
+    Stage sg;
+    gload(kt0, sg);
+    lstore(0, sg);
+    __syncthreads();
+    for (int kt = kt0; kt < KT; ++kt) {
+      if constexpr (I4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sw[j] = sg.sc[j];
+      }
+      if (kt + 1 < KT) gload(kt + 1, sg);
+      mma(kt);
+      if (kt + 1 < KT) lstore(((kt - kt0) & 1) ^ 1, sg);
+      __syncthreads();
+    }
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -431,22 +477,35 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
 
 template <int AK, int WK, bool LR>
 __global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
-  dq_body<AK, WK, LR, false>(dp);
+  dq_body<AK, WK, LR, false, false>(dp);
+}
+
+// Grids of at most one workgroup per compute unit (narrow weight groups,
+// split K) are bound by load latency: two K-tiles in flight.
+template <int AK, int WK, bool LR>
+__global__ __launch_bounds__(kThreads) void gemm_dq_deep_kernel(DqParams dp) {
+  dq_body<AK, WK, LR, false, true>(dp);
 }
 
 // The same GEMM with the activation operand read as the implicit im2col of a
 // 3x3 convolution.
-template <int AK, int WK>
+template <int AK, int WK, bool DEEP>
 __global__ __launch_bounds__(kThreads) void conv_dq_kernel(DqParams dp) {
-  dq_body<AK, WK, false, true>(dp);
+  dq_body<AK, WK, false, true, DEEP>(dp);
 }
 
 template <int AK, int WK>
 hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
+  // at most one workgroup per compute unit: two K-tiles in flight
+  const bool deep = (int64_t)grid.x * grid.y <= 256;
   if (p.g.cv_c > 0) {
     // implicit im2col of a quantized input (none for bf16 input)
     if constexpr (AK == K_BF) return hipErrorInvalidValue;
-    else conv_dq_kernel<AK, WK><<<grid, kThreads, 0, s>>>(p);
+    else if (deep) conv_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
+    else conv_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
+  } else if (deep) {
+    if (lr) gemm_dq_deep_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
+    else gemm_dq_deep_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
   } else if (lr) {
     gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
   } else {

@@ -115,6 +115,7 @@ CASES = [
     ("MXFP8", ("MXFP4", "NVFP4", "INT4"), 1, 6, 23, 640, 130, 4),    # K = 5760: slab accumulation
     ("MXFP8", ("NVFP4", "INT4"), 3, 1, 40, 128, 64, 5),              # one image row: dy taps all zero
     ("MXFP8", ("MXFP4",), 2, 12, 1, 256, 33, 6),                     # one image column
+    ("MXFP8", ("INT4",), 1, 48, 48, 128, 2000, 7),                   # 288 INT4 tiles: wide grid
 ]
 
 
@@ -125,7 +126,12 @@ def test_conv_matches_oracle(act_fmt, fmts, images, h, w, c, n, seed):
     assign = np.arange(n) % len(fmts)
     rng = np.random.default_rng(seed)
     bias = wl.f32_to_bf16_bits(rng.normal(0, 1, size=n).astype(np.float32)) if seed % 2 else None
-    _conv_check(lat, wt, act_fmt, fmts, assign, bias_bits=bias, tag=f"conv{seed}")
+    m = images * h * w
+    rows = None
+    if m > 1024:   # sampled pixels, corners and edges included
+        rows = np.unique(np.concatenate([[0, w - 1, m - w, m - 1, w, 2 * w - 1],
+                                         rng.choice(m, 64, replace=False)]))
+    _conv_check(lat, wt, act_fmt, fmts, assign, rows=rows, bias_bits=bias, tag=f"conv{seed}")
 
 
 def test_conv_single_group_without_permutation():

@@ -181,3 +181,29 @@ def test_int4_split_k(fa):
         assert np.all(y.float().cpu().numpy()[:, untouched] == -7.0)
         gu.check_gemm(y, a_deq, w_deq, alpha, bias=bias[perm], cols=perm, tag=f"{fa}xINT4 {tag}")
     assert torch.equal(ys[1], ys[2])
+
+
+@pytest.mark.parametrize("fa", ["MXFP8", "NVFP4", "MXFP4"])
+def test_int4_wide_grid_lowrank(fa):
+    """INT4 weights over more than one workgroup per compute unit (288 tiles:
+    one K-tile in flight per workgroup, where the small grids above keep two)
+    with bias and the rank-32 branch; sampled rows."""
+    import fp8_quantized_linear_mxq_amd as mxq
+    m, n, k = 2048, 2304, 256
+    gu.say(f"gemm {fa}xINT4 wide grid + low rank M={m} N={n} K={k}")
+    qa, qw = _operands(m, n, k, fa, "INT4", seed=123)
+    rng = np.random.default_rng(6)
+    r = 32
+    u = (rng.standard_normal((m, r)) * 4).astype(np.float32)
+    l2 = wl.bf16_to_f32(wl.f32_to_bf16_bits(rng.normal(0, 0.02, (r, n)).astype(np.float32)))
+    bias = wl.bf16_to_f32(wl.f32_to_bf16_bits(rng.normal(0, 1, n).astype(np.float32)))
+    y = mxq.gemm(gu.qtensor_from_oracle(qa, m, k), gu.qtensor_from_oracle(qw, n, k),
+                 u=gu.to_dev_f32(u),
+                 l2t=gu.to_dev_bf16(wl.f32_to_bf16_bits(np.ascontiguousarray(l2.T))),
+                 bias=gu.to_dev_bf16(wl.f32_to_bf16_bits(bias)))
+    rows = np.unique(np.concatenate([rng.choice(m, 64, replace=False), [0, m - 1]]))
+    alpha = gu.alpha_of(qa, qw)
+    a_deq = np.hstack([gu.dequant_a_for_gemm(qa)[rows], u[rows].astype(np.float64)])
+    w_deq = np.hstack([gu.dequant_w_for_gemm(qw), l2.T.astype(np.float64) / alpha])
+    ratio = gu.check_gemm(y, a_deq, w_deq, alpha, bias=bias, rows=rows, tag=f"{fa}xINT4 wide")
+    gu.say(f"  worst err/tol {ratio:.3g}")
