@@ -401,8 +401,11 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
   epilogue_tr<LR, TM, TN>(p, acc, alpha, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
 }
 
+// Slabbed tiles run two workgroups per CU, except with bf16 activations,
+// whose three LDS stages take 123 KB.
 template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR>
-__global__ __launch_bounds__(128 * WGM, SLAB ? 2 : 1) void gemm_dqp_kernel(DqpParams dp) {
+__global__ __launch_bounds__(128 * WGM, (SLAB && AK != K_BF) ? 2 : 1) void gemm_dqp_kernel(
+    DqpParams dp) {
   dqp_body<AK, WK, TM, TN, WGM, SLAB, LR, false>(dp);
 }
 
