@@ -76,3 +76,71 @@ def test_graph_replay_matches_eager(fa, fw, had, rank):
         got = snapshot(*cap)
         for a, b in zip(got, want):
             assert torch.equal(a, b), f"replay {rep}: a graph output differs from eager"
+
+
+def _replay_check(run, outputs, tag):
+    """Capture run() in a graph; every replay (outputs cleared first, eager
+    work and synchronizations in between) equals the eager result."""
+    import torch
+    run()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outputs]
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outputs:
+            t.fill_(-3.0)
+        run()
+        torch.cuda.synchronize()
+        for t in outputs:
+            t.fill_(-5.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outputs, want):
+            assert torch.equal(a, b), f"{tag} replay {rep}: a graph output differs from eager"
+
+
+def test_graph_replay_conv_and_split_k():
+    """The implicit-im2col convolution with a narrow INT4 group (split K:
+    partial sums in the workspace, then the reduction kernel) and an NVFP4
+    group, captured and replayed."""
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    gu.say("graph replay: implicit-im2col convolution, INT4 split K + NVFP4 group")
+    rng = np.random.default_rng(21)
+    h, w, c = 12, 14, 256
+    lat = wl.f32_to_bf16_bits((rng.standard_t(3, size=(h * w, c)) * 3).astype(np.float32))
+    qx = mxq.quantize(gu.to_dev_bf16(lat), mxq.MXFP8)
+    wt = gu.to_dev_f32(wl.mixed_weights(9 * c, 84, seed=3))
+    g_int4 = mxq.quantize(wt[:20].contiguous(), mxq.INT4)
+    g_nv = mxq.quantize(wt[20:].contiguous(), mxq.NVFP4)
+    perm = torch.from_numpy(rng.permutation(84).astype(np.int32)).cuda()
+    assert mxq.workspace_size(mxq.OP_GEMM, h * w, 20, mxq.INT4) > 0
+    ws = torch.empty((mxq.workspace_size(mxq.OP_GEMM, h * w, 20, mxq.INT4),), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty((h * w, 84), dtype=torch.bfloat16, device="cuda")
+    _replay_check(lambda: mxq.conv3x3_gemm_mixed(qx, h, w, [g_int4, g_nv], perm, 84, out=y,
+                                                 workspace=ws), [y], "conv")
+
+
+def test_graph_replay_w4a16():
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    gu.say("graph replay: bf16 activations x INT4 and NVFP4 weights")
+    rng = np.random.default_rng(22)
+    m, k, n = 260, 640, 300
+    x = gu.to_dev_bf16(wl.f32_to_bf16_bits((rng.standard_t(3, size=(m, k)) * 2).astype(np.float32)))
+    wf = gu.to_dev_f32(rng.normal(0, 0.02, size=(n, k)).astype(np.float32))
+    a = mxq.bf16_operand(x)
+    q4, qn = mxq.quantize(wf, mxq.INT4), mxq.quantize(wf, mxq.NVFP4)
+    y4 = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    yn = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        mxq.gemm(a, q4, out=y4, workspace=False)
+        mxq.gemm(a, qn, out=yn)
+    _replay_check(run, [y4, yn], "w4a16")
