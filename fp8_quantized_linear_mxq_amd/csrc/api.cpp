@@ -301,8 +301,9 @@ mxq_status mxq_conv3x3_gemm_mixed(const mxq_qtensor* x, int64_t height, int64_t 
   if (workspace && !aligned(workspace, 16)) return MXQ_ERR_ALIGNMENT;
   if (height > INT32_MAX / width) return MXQ_ERR_SHAPE;
   const int64_t C = x->cols, hw = height * width;
-  // a K-tile (128) never spans two taps; pixels are whole images
-  if (C % 128 || x->rows % hw) return MXQ_ERR_SHAPE;
+  // a K-tile (128) never spans two taps; pixels are whole images; the
+  // kernels' tap lookup is exact up to 2**20 channels
+  if (C % 128 || x->rows % hw || C > (1 << 20)) return MXQ_ERR_SHAPE;
   if (x->rows > INT32_MAX || 9 * C > INT32_MAX || n_out > INT32_MAX) return MXQ_ERR_SHAPE;
   int64_t total = 0;
   for (int g = 0; g < n_groups; ++g) {

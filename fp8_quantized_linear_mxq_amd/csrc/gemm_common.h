@@ -36,34 +36,54 @@ struct GemmP {
   int cv_h, cv_w, cv_c;
 };
 
-// The tap of K-tile kt (bk elements wide) of an implicit-im2col operand: the
-// pixel offsets (dy, dx), the K-tile's index inside the channel row, and the
-// row shift dy * width + dx.
-struct ConvTap {
-  int dy, dx, kc, shift;
+// K-tiles per tap (cv_c / bk) and ceil(2**32 / tiles): floor(kt / tiles) is
+// then one multiply, exact while kt * tiles < 2**32, which holds for every
+// K-tile when cv_c <= 2**20 (kt < 9 * tiles, tiles <= 2**14).
+struct ConvDiv {
+  uint32_t tiles;
+  uint64_t magic;
 };
 
-__device__ __forceinline__ ConvTap conv_tap(const GemmP& p, int kt, int bk) {
-  const int tiles = p.cv_c / bk;   // K-tiles per tap
-  const int tap = kt / tiles;
+__device__ __forceinline__ ConvDiv conv_div(const GemmP& p, int bk) {
+  ConvDiv d;
+  d.tiles = (uint32_t)(p.cv_c / bk);
+  d.magic = ((1ull << 32) + d.tiles - 1) / d.tiles;
+  return d;
+}
+
+// The tap (ky * 3 + kx) of K-tile kt of an implicit-im2col operand, its
+// pixel offsets (dy, dx) = (ky - 1, kx - 1), the K-tile's index inside the
+// channel row, and the row shift dy * width + dx.
+struct ConvTap {
+  int tap, dy, dx, kc, shift;
+};
+
+__device__ __forceinline__ ConvTap conv_tap(const GemmP& p, const ConvDiv& d, int kt) {
   ConvTap t;
-  t.kc = kt - tap * tiles;
-  t.dy = tap / 3 - 1;
-  t.dx = tap - 3 * (tap / 3) - 1;
+  t.tap = (int)(((uint64_t)(uint32_t)kt * d.magic) >> 32);
+  t.kc = kt - t.tap * (int)d.tiles;
+  t.dy = t.tap / 3 - 1;
+  t.dx = t.tap - 3 * (t.tap / 3) - 1;
   t.shift = t.dy * p.cv_w + t.dx;
   return t;
 }
 
-// Pixel coordinates of GEMM row `row` of an implicit-im2col operand.
-__device__ __forceinline__ void conv_pixel(const GemmP& p, int row, int& y, int& x) {
+// Bit t of the mask is set when tap t of GEMM row `row` reads a pixel inside
+// the image (computed once per row; a K-tile then tests one bit).
+__device__ __forceinline__ uint32_t conv_mask(const GemmP& p, int row) {
   const int hw = row % (p.cv_h * p.cv_w);
-  y = hw / p.cv_w;
-  x = hw - y * p.cv_w;
+  const int y = hw / p.cv_w, x = hw - (hw / p.cv_w) * p.cv_w;
+  uint32_t m = 0;
+#pragma unroll
+  for (int t = 0; t < 9; ++t) {
+    const int yy = y + t / 3 - 1, xx = x + t % 3 - 1;
+    m |= ((unsigned)yy < (unsigned)p.cv_h && (unsigned)xx < (unsigned)p.cv_w) ? (1u << t) : 0u;
+  }
+  return m;
 }
 
-// Whether pixel (y, x) shifted by the tap lies inside the image.
-__device__ __forceinline__ bool conv_inside(const GemmP& p, const ConvTap& t, int y, int x) {
-  return (unsigned)(y + t.dy) < (unsigned)p.cv_h && (unsigned)(x + t.dx) < (unsigned)p.cv_w;
+__device__ __forceinline__ bool conv_inside(uint32_t mask, const ConvTap& t) {
+  return (mask >> t.tap) & 1u;
 }
 
 __device__ __forceinline__ int remap_tile(int bid, int total) {

@@ -232,12 +232,14 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
     }
   }
   // Implicit im2col: pixel coordinates of this thread's activation rows.
-  int cv_y[2] = {0, 0}, cv_x[2] = {0, 0};
+  uint32_t cv_m[2] = {0u, 0u};   // taps inside the image (conv_mask)
+  ConvDiv cv_div{};
   if constexpr (CONV) {
+    cv_div = conv_div(p, BK);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = AK == K_MX8 ? m0 + ar8[i] : m0 + fr;
-      conv_pixel(p, row < p.M ? row : 0, cv_y[i], cv_x[i]);
+      cv_m[i] = conv_mask(p, row < p.M ? row : 0);
     }
   }
   // INT4 weights: this lane's output columns' fp32 block scales.
@@ -263,11 +265,11 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
   auto gload = [&](int kt, Stage& S) __attribute__((always_inline)) {
     wl.load(kt, S.w);
     if constexpr (CONV) {
-      const ConvTap tp = conv_tap(p, kt, BK);
+      const ConvTap tp = conv_tap(p, cv_div, kt);
       if constexpr (AK == K_MX8) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const bool in = conv_inside(p, tp, cv_y[i], cv_x[i]);
+          const bool in = conv_inside(cv_m[i], tp);
           S.a16[i] = (a_ok8[i] && in)
                          ? *reinterpret_cast<const uint4*>(a_code8[i] + (int64_t)tp.shift * p.lda +
                                                            (int64_t)tp.kc * 64)
@@ -277,7 +279,7 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
           S.a8s[i] = in ? v : 0u;
         }
       } else {
-        al.load_conv(tp.kc, tp.shift, p.lda, p.ldas, conv_inside(p, tp, cv_y[0], cv_x[0]), S.a);
+        al.load_conv(tp.kc, tp.shift, p.lda, p.ldas, conv_inside(cv_m[0], tp), S.a);
       }
     } else if constexpr (AK == K_MX8) {
 #pragma unroll

@@ -192,10 +192,12 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
   constexpr int S_DA = TBM * SBA / 4, S_D = S_DA + TBN * SBW / 4;
   constexpr int S_LD = (S_D + 64 * NW - 1) / (64 * NW);
   const uint8_t* cv_code[CONV ? A_LD : 1];
-  int cv_y[CONV ? A_LD : 1], cv_x[CONV ? A_LD : 1];
+  uint32_t cv_m[CONV ? A_LD : 1];     // taps inside the image (conv_mask)
   const uint8_t* cv_scl[CONV ? S_LD : 1];
-  int cv_sy[CONV ? S_LD : 1], cv_sx[CONV ? S_LD : 1];
+  uint32_t cv_sm[CONV ? S_LD : 1];
+  ConvDiv cv_div{};
   if constexpr (CONV) {
+    cv_div = conv_div(p, BK);
     constexpr int TOTAL = TBM * A_CH / 64;
 #pragma unroll
     for (int t = 0; t < A_LD; ++t) {
@@ -205,8 +207,7 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
       const int r = L / A_CH, lc = (L % A_CH) ^ swz<A_CH>(r);
       const int grow = m0 + r < p.M ? m0 + r : p.M - 1;
       cv_code[t] = p.a + (int64_t)grow * p.lda + lc * 16;
-      conv_pixel(p, grow, cv_y[t], cv_x[t]);
-      if (!real) cv_y[t] = -(1 << 24);
+      cv_m[t] = real ? conv_mask(p, grow) : 0u;
     }
 #pragma unroll
     for (int t = 0; t < S_LD; ++t) {
@@ -214,8 +215,7 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
       const int dd = d < S_DA ? d : 0;
       const int grow = m0 + dd / (SBA / 4) < p.M ? m0 + dd / (SBA / 4) : p.M - 1;
       cv_scl[t] = p.as + (int64_t)grow * p.ldas + (dd % (SBA / 4)) * 4;
-      conv_pixel(p, grow, cv_sy[t], cv_sx[t]);
-      if (d >= S_DA) cv_sy[t] = -(1 << 24);
+      cv_sm[t] = d < S_DA ? conv_mask(p, grow) : 0u;
     }
   }
 
@@ -224,14 +224,14 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
     kt = past ? KT - 1 : kt;
     uint8_t* pad = st + A_STAGE + W_STAGE + S_STAGE;
     if constexpr (CONV) {
-      const ConvTap tp = conv_tap(p, kt, BK);
+      const ConvTap tp = conv_tap(p, cv_div, kt);
       const int64_t off = (int64_t)tp.shift * p.lda + tp.kc * A_RB;
       constexpr int TOTAL = TBM * A_CH / 64;
 #pragma unroll
       for (int t = 0; t < A_LD; ++t) {
         const int idx = t * NW + wave;
         const bool real = (TOTAL % NW == 0) || idx < TOTAL;
-        const bool in = !past && conv_inside(p, tp, cv_y[t], cv_x[t]);
+        const bool in = !past && conv_inside(cv_m[t], tp);
         const uint8_t* src = in ? cv_code[t] + off : g_zero16;
         uint8_t* dst = real ? st + idx * 64 * 16 : pad;
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
@@ -246,7 +246,7 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
         const int d = slot0 + lane;
         const uint8_t* src;
         if (d < S_DA) {
-          src = conv_inside(p, tp, cv_sy[t], cv_sx[t]) ? cv_scl[t] + soff : g_zero16;
+          src = conv_inside(cv_sm[t], tp) ? cv_scl[t] + soff : g_zero16;
         } else if (d < S_D) {
           const int e = d - S_DA;
           int r = n0 + e / (SBW / 4);

@@ -216,7 +216,7 @@ mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int
  *
  *  x           quantized input [images * height * width][C] (pixel rows in
  *              row-major image, y, x order; C channels): MXFP8, NVFP4 or
- *              MXFP4 (not bf16).  C must be a multiple of 128.
+ *              MXFP4 (not bf16).  C must be a multiple of 128, at most 2**20.
  *  height, width  the spatial size of each image (> 0); x->rows must be a
  *              multiple of height * width.
  *  w_groups, n_groups, w_perm  weight groups as in mxq_gemm_mixed, each
