@@ -178,7 +178,7 @@ struct Fp4Loader {
   }
 };
 
-template <int AK, int WK, bool LR, bool CONV, bool DEEP>
+template <int AK, int WK, bool LR, bool CONV, bool DEEP, bool SLAB>
 __device__ __forceinline__ void dq_body(const DqParams& dp) {
   const GemmP& p = dp.g;
   constexpr bool FP16 = (AK == K_NV && WK == K_NV);
@@ -344,14 +344,19 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
 
   // column tiles of this wave that hold any of the N columns (wave-uniform)
   const int live_j = n0 + wn * 64 + 32 < p.N ? 2 : (n0 + wn * 64 < p.N ? 1 : 0);
-  v16f acc[2][2], tot[2][2];
+  // fp32 slabs of kSlabTiles K-tiles (S21) where a workgroup's share of K
+  // is longer than one slab
+  v16f acc[2][2], tot[SLAB ? 2 : 1][SLAB ? 2 : 1];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[i][j] = v16f{};
-      tot[i][j] = v16f{};
-    }
+    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+  if constexpr (SLAB) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) tot[i][j] = v16f{};
+  }
 
   // Multiply K-tile kt from LDS buffer (kt - kt0) & 1 (INT4 block scales in sw).
   auto mma = [&](int kt) __attribute__((always_inline)) {
@@ -396,14 +401,16 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
 #pragma unroll
           for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[ks][i], bf[ks][j], acc[i][j]);
     }
-    if ((kt - kt0 + 1) % kSlabTiles == 0) {
+    if constexpr (SLAB) {
+      if ((kt - kt0 + 1) % kSlabTiles == 0) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          tot[i][j] += acc[i][j];
-          acc[i][j] = v16f{};
-        }
+          for (int j = 0; j < 2; ++j) {
+            tot[i][j] += acc[i][j];
+            acc[i][j] = v16f{};
+          }
+      }
     }
   };
 
@@ -449,10 +456,12 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
       __syncthreads();
     }
   }
+  if constexpr (SLAB) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] += tot[i][j];
+      for (int j = 0; j < 2; ++j) acc[i][j] += tot[i][j];
+  }
   if (dp.part) {
     // split K: this split's fp32 sums (C layout: lane column l32, rows
     // 8(q/4) + 4*half + q%4 of each 32x32 tile); launch_splitk_reduce finishes
@@ -477,23 +486,25 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
   epilogue<LR>(p, acc, alpha, m0, n0, wm, wn, lane);
 }
 
-template <int AK, int WK, bool LR>
-__global__ __launch_bounds__(kThreads) void gemm_dq_kernel(DqParams dp) {
-  dq_body<AK, WK, LR, false, false>(dp);
+// Without slabs (a share of K of at most kSlabTiles K-tiles) the registers
+// allow two workgroups per compute unit.
+template <int AK, int WK, bool LR, bool SLAB>
+__global__ __launch_bounds__(kThreads, SLAB ? 1 : 2) void gemm_dq_kernel(DqParams dp) {
+  dq_body<AK, WK, LR, false, false, SLAB>(dp);
 }
 
 // Grids of at most one workgroup per compute unit (narrow weight groups,
 // split K) are bound by load latency: two K-tiles in flight.
 template <int AK, int WK, bool LR>
 __global__ __launch_bounds__(kThreads) void gemm_dq_deep_kernel(DqParams dp) {
-  dq_body<AK, WK, LR, false, true>(dp);
+  dq_body<AK, WK, LR, false, true, true>(dp);
 }
 
 // The same GEMM with the activation operand read as the implicit im2col of a
 // 3x3 convolution.
 template <int AK, int WK, bool DEEP>
 __global__ __launch_bounds__(kThreads) void conv_dq_kernel(DqParams dp) {
-  dq_body<AK, WK, false, true, DEEP>(dp);
+  dq_body<AK, WK, false, true, DEEP, true>(dp);
 }
 
 template <int AK, int WK>
@@ -508,10 +519,15 @@ hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
   } else if (deep) {
     if (lr) gemm_dq_deep_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
     else gemm_dq_deep_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
-  } else if (lr) {
-    gemm_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
   } else {
-    gemm_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
+    const int share = p.part ? p.kt_split : p.g.K / BK;   // K-tiles per workgroup
+    if (share > kSlabTiles) {
+      if (lr) gemm_dq_kernel<AK, WK, true, true><<<grid, kThreads, 0, s>>>(p);
+      else gemm_dq_kernel<AK, WK, false, true><<<grid, kThreads, 0, s>>>(p);
+    } else {
+      if (lr) gemm_dq_kernel<AK, WK, true, false><<<grid, kThreads, 0, s>>>(p);
+      else gemm_dq_kernel<AK, WK, false, false><<<grid, kThreads, 0, s>>>(p);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.part) return e;

@@ -183,13 +183,15 @@ def test_int4_split_k(fa):
     assert torch.equal(ys[1], ys[2])
 
 
-@pytest.mark.parametrize("fa", ["MXFP8", "NVFP4", "MXFP4"])
-def test_int4_wide_grid_lowrank(fa):
+@pytest.mark.parametrize("fa,k", [("MXFP8", 256), ("NVFP4", 256), ("MXFP4", 256),
+                                  ("MXFP8", 4224)])
+def test_int4_wide_grid_lowrank(fa, k):
     """INT4 weights over more than one workgroup per compute unit (288 tiles:
     one K-tile in flight per workgroup, where the small grids above keep two)
-    with bias and the rank-32 branch; sampled rows."""
+    with bias and the rank-32 branch; K = 256 runs without fp32 slabs (two
+    workgroups per compute unit), K = 4224 with them; sampled rows."""
     import fp8_quantized_linear_mxq_amd as mxq
-    m, n, k = 2048, 2304, 256
+    m, n = 2048, 2304
     gu.say(f"gemm {fa}xINT4 wide grid + low rank M={m} N={n} K={k}")
     qa, qw = _operands(m, n, k, fa, "INT4", seed=123)
     rng = np.random.default_rng(6)
