@@ -502,26 +502,28 @@ __global__ __launch_bounds__(kThreads) void gemm_dq_deep_kernel(DqParams dp) {
 
 // The same GEMM with the activation operand read as the implicit im2col of a
 // 3x3 convolution.
-template <int AK, int WK, bool DEEP>
-__global__ __launch_bounds__(kThreads) void conv_dq_kernel(DqParams dp) {
-  dq_body<AK, WK, false, true, DEEP, true>(dp);
+template <int AK, int WK, bool DEEP, bool SLAB>
+__global__ __launch_bounds__(kThreads, SLAB ? 1 : 2) void conv_dq_kernel(DqParams dp) {
+  dq_body<AK, WK, false, true, DEEP, SLAB>(dp);
 }
 
 template <int AK, int WK>
 hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
   // at most one workgroup per compute unit: two K-tiles in flight
   const bool deep = (int64_t)grid.x * grid.y <= 256;
+  const int share = p.part ? p.kt_split : p.g.K / BK;   // K-tiles per workgroup
+  const bool slab = share > kSlabTiles;
   if (p.g.cv_c > 0) {
     // implicit im2col of a quantized input (none for bf16 input)
     if constexpr (AK == K_BF) return hipErrorInvalidValue;
-    else if (deep) conv_dq_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
-    else conv_dq_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
+    else if (deep) conv_dq_kernel<AK, WK, true, true><<<grid, kThreads, 0, s>>>(p);
+    else if (slab) conv_dq_kernel<AK, WK, false, true><<<grid, kThreads, 0, s>>>(p);
+    else conv_dq_kernel<AK, WK, false, false><<<grid, kThreads, 0, s>>>(p);
   } else if (deep) {
     if (lr) gemm_dq_deep_kernel<AK, WK, true><<<grid, kThreads, 0, s>>>(p);
     else gemm_dq_deep_kernel<AK, WK, false><<<grid, kThreads, 0, s>>>(p);
   } else {
-    const int share = p.part ? p.kt_split : p.g.K / BK;   // K-tiles per workgroup
-    if (share > kSlabTiles) {
+    if (slab) {
       if (lr) gemm_dq_kernel<AK, WK, true, true><<<grid, kThreads, 0, s>>>(p);
       else gemm_dq_kernel<AK, WK, false, true><<<grid, kThreads, 0, s>>>(p);
     } else {
@@ -542,16 +544,28 @@ hipError_t dispatch_w(int w_fmt, bool lr, dim3 grid, const DqParams& p, hipStrea
 
 }  // namespace
 
-int dq_splits(int64_t M, int64_t N) {
+constexpr int kMaxSplits = 16;
+
+// K splits of an M x N x K problem: narrow weight groups (at most 128
+// output tiles) split K to fill the chip (about 256 workgroups, at most 4
+// splits), and further, up to 16 splits, into shares of at most kSlabTiles
+// K-tiles: those run without fp32 slabs at two workgroups per CU.
+int dq_splits(int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (tiles <= 0 || tiles > 128) return 1;
-  const int64_t s = 256 / tiles;
-  return (int)(s > 4 ? 4 : s);
+  const int64_t kt = K / BK;
+  if (tiles <= 0 || tiles > 128 || kt < 2) return 1;
+  int64_t s = 256 / tiles;
+  s = s > 4 ? 4 : s;
+  const int64_t s_slab = (kt + kSlabTiles - 1) / kSlabTiles;
+  if (s_slab > s) s = s_slab < kMaxSplits ? s_slab : kMaxSplits;
+  return (int)(s < kt ? s : kt);
 }
 
+// Workspace for any K: narrow groups may take up to kMaxSplits fp32 partials.
 int64_t gemm_dq_workspace(int64_t M, int64_t N) {
-  const int s = dq_splits(M, N);
-  return s > 1 ? (int64_t)s * M * N * 4 : 0;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles <= 0 || tiles > 128) return 0;
+  return (int64_t)kMaxSplits * M * N * 4;
 }
 
 hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s) {
@@ -575,8 +589,16 @@ hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s) {
   // Too few tiles to fill the chip (narrow weight groups): split K over
   // blockIdx.y into fp32 partials in the workspace, then sum them in split
   // order (deterministic) in a second kernel.  Not with the low-rank branch.
-  const int splits = lr ? 1 : dq_splits(a.M, a.N);
-  if (splits > 1 && a.ws && a.ws_bytes >= gemm_dq_workspace(a.M, a.N)) {
+  // A smaller workspace takes as many splits as fit.
+  int splits = lr ? 1 : dq_splits(a.M, a.N, a.K);
+  const int64_t per_split = a.M * a.N * 4;
+  if (splits > 1 && a.ws && per_split > 0) {
+    const int64_t fit = a.ws_bytes / per_split;
+    if (fit < splits) splits = (int)fit;
+  } else {
+    splits = 1;
+  }
+  if (splits > 1) {
     const int kt = (int)(a.K / BK);
     dp.kt_split = (kt + splits - 1) / splits;
     dp.part = a.ws;

@@ -59,9 +59,9 @@ struct GemmArgs {
   int64_t cv_h, cv_w, cv_c;
 };
 hipError_t launch_gemm_mx(const GemmArgs& a, hipStream_t s);
-// INT4-row route: K splits for an M x N problem (1 = none) and the
-// workspace bytes they need.
-int dq_splits(int64_t M, int64_t N);
+// INT4-row route: K splits for an M x N x K problem (1 = none) and the
+// workspace bytes that cover the splits of any K.
+int dq_splits(int64_t M, int64_t N, int64_t K);
 int64_t gemm_dq_workspace(int64_t M, int64_t N);
 hipError_t launch_gemm_dq(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_dqp(const GemmArgs& a, hipStream_t s);

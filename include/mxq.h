@@ -172,13 +172,15 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
  *  bias        optional device bf16 [n_out], indexed by output column.
  *  out         device bf16 [M][ld_out], n_out columns; 4-byte aligned.
  *  workspace   optional (NULL, or 16-byte aligned device memory of ws_bytes):
- *              with at least mxq_workspace_size(MXQ_OP_GEMM, M, N, w->fmt)
- *              bytes, INT4 weights too narrow to fill the GPU (few output
- *              tiles) split K into fp32 partial sums there, which a second
- *              kernel adds in a fixed order (results are deterministic; they
- *              may differ from the unsplit sum by fp32 rounding, within the
- *              same error bound).  Otherwise, and for every other route and
- *              with a low-rank branch, it is unused.
+ *              INT4 weights too narrow to fill the GPU (at most 128 output
+ *              tiles of 128 x 128) split K into fp32 partial sums there (up
+ *              to 16 splits of M * N floats; mxq_workspace_size(MXQ_OP_GEMM,
+ *              M, N, w->fmt) bytes cover every K, and a smaller workspace
+ *              takes as many splits as fit), which a second kernel adds in a
+ *              fixed order (results are deterministic for a given workspace
+ *              size; they may differ from the unsplit sum by fp32 rounding,
+ *              within the same error bound).  Otherwise, and for every other
+ *              route and with a low-rank branch, it is unused.
  * Requirements: a->cols == w->cols == K, K a multiple of 128.
  * M or N of 0 is a no-op.  Accumulation is fp32; long K is summed in slabs.
  */

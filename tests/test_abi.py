@@ -51,8 +51,9 @@ def test_workspace_sizes(lib):
     assert _lib.workspace_size(_lib.OP_GEMM, 4096, 4608, _lib.MXFP4) == 0
     assert _lib.workspace_size(_lib.OP_GEMM, 256, 1152, _lib.MXFP4) == 0
     assert _lib.workspace_size(_lib.OP_GEMM, 4096, 4608, _lib.INT4) == 0
-    assert _lib.workspace_size(_lib.OP_GEMM, 16384, 20, _lib.INT4) == 2 * 16384 * 20 * 4
-    assert _lib.workspace_size(_lib.OP_GEMM, 200, 300, _lib.INT4) == 4 * 200 * 300 * 4
+    assert _lib.workspace_size(_lib.OP_GEMM, 16384, 20, _lib.INT4) == 16 * 16384 * 20 * 4
+    assert _lib.workspace_size(_lib.OP_GEMM, 200, 300, _lib.INT4) == 16 * 200 * 300 * 4
+    assert _lib.workspace_size(_lib.OP_GEMM, 16384, 200, _lib.INT4) == 0   # 256 tiles
 
 
 def test_act_format_lookup_matches_oracle(lib):

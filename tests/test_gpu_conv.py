@@ -116,6 +116,7 @@ CASES = [
     ("MXFP8", ("NVFP4", "INT4"), 3, 1, 40, 128, 64, 5),              # one image row: dy taps all zero
     ("MXFP8", ("MXFP4",), 2, 12, 1, 256, 33, 6),                     # one image column
     ("MXFP8", ("INT4",), 1, 48, 48, 128, 2000, 7),                   # 288 INT4 tiles: wide grid
+    ("MXFP8", ("INT4",), 1, 48, 48, 384, 2000, 8),                   # wide grid, 54 K-tiles: slabs
 ]
 
 

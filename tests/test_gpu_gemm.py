@@ -154,15 +154,14 @@ def test_int4_split_k(fa):
     sums when a workspace is given, summed in a fixed order by a second
     kernel with the alpha, bias and column map of the epilogue.  Both paths
     meet the tolerance; the split one is deterministic.  K = 4224 gives 66
-    K-tiles of 64 over four splits (17, 17, 17, 15), each with its own fp32
-    slabs."""
+    K-tiles of 64 over four splits (17, 17, 17, 15)."""
     import torch
     import fp8_quantized_linear_mxq_amd as mxq
     m, n, k = 300, 20, 4224
     gu.say(f"gemm {fa}xINT4 split K M={m} N={n} K={k}")
     qa, qw = _operands(m, n, k, fa, "INT4", seed=77)
     a_dev, w_dev = gu.qtensor_from_oracle(qa, m, k), gu.qtensor_from_oracle(qw, n, k)
-    assert mxq.workspace_size(mxq.OP_GEMM, m, n, mxq.INT4) == 4 * m * n * 4
+    assert mxq.workspace_size(mxq.OP_GEMM, m, n, mxq.INT4) == 16 * m * n * 4
     rng = np.random.default_rng(9)
     n_out = 40
     perm = rng.permutation(n_out)[:n].astype(np.int32)
