@@ -72,10 +72,19 @@ def quantize_bytes(w: wl.Workload, cols: int | None = None) -> int:
 
 def mixed_weights(w: wl.Workload, mxq, torch):
     """Per-output-channel format choice on the conv weight and its groups,
-    quantized once (outside the timed region)."""
+    quantized once (outside the timed region).  Also returns the format
+    choice's average duration (HIP events around five further calls)."""
     w0 = torch.from_numpy(wl.weights(w)).cuda()
     _, _, perm, counts, g = mxq.select_format(w0)
     cnt = counts.cpu().tolist()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        mxq.select_format(w0)
+    e1.record()
+    torch.cuda.synchronize()
+    select_us = e0.elapsed_time(e1) / 5 * 1e3
     groups, off = [], 0
     for ci, fmt in enumerate((mxq.INT4, mxq.MXFP4, mxq.NVFP4)):
         rows = perm[off:off + cnt[ci]].long()
@@ -84,7 +93,7 @@ def mixed_weights(w: wl.Workload, mxq, torch):
                       if cnt[ci] else mxq.empty_qtensor(fmt, 0, w.k))
         off += cnt[ci]
     del w0
-    return groups, perm, cnt
+    return groups, perm, cnt, select_us
 
 
 def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None, conv="implicit"):
@@ -96,7 +105,7 @@ def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None, conv="implici
         act = lat.reshape(-1, lat.shape[2]) if conv == "implicit" else wl.im2col(lat)
         x0 = torch.from_numpy(np.ascontiguousarray(act).view(np.int16)).view(torch.bfloat16).cuda()
         del act, lat
-        groups, perm, _ = mixed
+        groups, perm = mixed[0], mixed[1]
         ws_n = max([mxq.workspace_size(mxq.OP_GEMM, w.m, g.rows, g.fmt) for g in groups] + [16])
         sets = []
         for i in range(n_sets):
@@ -307,6 +316,23 @@ def main() -> int:
     q_ms = None if bf16_act else graph_avg_ms(torch, [lambda s=s: quant(s) for s in sets],
                                               args.steps)
     g_ms = graph_avg_ms(torch, [lambda s=s: gemm(s) for s in sets], args.steps)
+    group_us = {}
+    if mixed:
+        # each format group's GEMM alone (same graph timing, output columns
+        # through the group's slice of the permutation)
+        off = 0
+        for name, grp in zip(("INT4", "MXFP4", "NVFP4"), mixed[0]):
+            if grp.rows:
+                cols = mixed[1][off:off + grp.rows]
+                if implicit:
+                    one = [lambda s=s: mxq.conv3x3_gemm_mixed(s["qa"], lat_h, lat_w, [grp], cols,
+                                                              w.n, out=s["out"], workspace=s["ws"])
+                           for s in sets]
+                else:
+                    one = [lambda s=s: mxq.gemm(s["qa"], grp, n_out=w.n, w_out_col=cols,
+                                                out=s["out"], workspace=s["ws"]) for s in sets]
+                group_us[name] = round(graph_avg_ms(torch, one, args.steps // 4 or 1) * 1e3, 1)
+            off += grp.rows
     if args.copy_probe:
         a = torch.empty((1 << 28,), dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -358,6 +384,8 @@ def main() -> int:
     if mixed:
         rec["config"]["weight_groups"] = {"INT4": mixed[2][0], "MXFP4": mixed[2][1],
                                           "NVFP4": mixed[2][2]}
+        rec["format_choice_us"] = round(mixed[3], 1)
+        rec["group_gemm_us"] = group_us
         rec["config"]["conv"] = ("implicit im2col: quantize the 128x128x2560 input once, "
                                  "gather the 3x3 taps in the GEMM") if implicit else \
             "explicit im2col: quantize the 16384x23040 matrix"
