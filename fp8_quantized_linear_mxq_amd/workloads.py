@@ -23,6 +23,7 @@ shapes):
                16384 x 23040 x 1280, MXFP8 activations, per-row weight formats
   w4a16_mlp    4096 x 1152 x 4608, the w4a8_mlp activations kept in bf16
                (4-bit weights, 16-bit activations) against INT4 weights
+  w4a16_mx_mlp the same against MXFP4 weights
 Weights are N(0, 0.02) float32 master copies.
 """
 
@@ -77,6 +78,7 @@ WORKLOADS = {
                                "MIXED", seed=4,
                                extra={"latent": (128, 128, 2560), "ksize": 3}),
     "w4a16_mlp": Workload("w4a16_mlp", 4096, 1152, 4608, "bf16", "BF16", "INT4", seed=1),
+    "w4a16_mx_mlp": Workload("w4a16_mx_mlp", 4096, 1152, 4608, "bf16", "BF16", "MXFP4", seed=1),
 }
 
 
@@ -99,7 +101,7 @@ def activations(wl: Workload, rows: int | None = None) -> np.ndarray:
     if wl.name == "w4a4_small":
         a = st[0].standard_t(4, size=(m, wl.k)) * 1.0
         return a.astype(np.float32)
-    if wl.name in ("w4a8_mlp", "w4a16_mlp"):
+    if wl.name in ("w4a8_mlp", "w4a16_mlp", "w4a16_mx_mlp"):
         a = st[0].standard_t(3, size=(m, wl.k))
         n_hot = int(round(0.005 * wl.k))
         hot = st[4].choice(wl.k, size=n_hot, replace=False)

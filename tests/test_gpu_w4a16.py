@@ -90,13 +90,14 @@ def test_w4a16_rejects():
     assert ei.value.status == 4
 
 
-def test_w4a16_workload_full_size():
-    """The benchmarked layer at full size (4096 x 1152 x 4608, bf16
-    activations, INT4 weights quantized on the GPU): weight codes and scales
-    bit-exact, outputs checked on sampled rows."""
+@pytest.mark.parametrize("name", ["w4a16_mlp", "w4a16_mx_mlp"])
+def test_w4a16_workload_full_size(name):
+    """The benchmarked layers at full size (4096 x 1152 x 4608, bf16
+    activations, INT4 or MXFP4 weights quantized on the GPU): weight codes
+    and scales bit-exact, outputs checked on sampled rows."""
     import torch
     import fp8_quantized_linear_mxq_amd as mxq
-    w = wl.WORKLOADS["w4a16_mlp"]
+    w = wl.WORKLOADS[name]
     gu.say(f"workload {w.name}: M={w.m} K={w.k} N={w.n} bf16 x {w.w_fmt}")
     act = wl.activations(w)
     wt = wl.weights(w)
