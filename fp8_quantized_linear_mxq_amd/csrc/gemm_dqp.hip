@@ -478,11 +478,15 @@ hipError_t launch_tiles(bool lr, const DqpParams& dp, hipStream_t s) {
 template <int AK, int WK>
 hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
   if constexpr (AK == K_BF) {
-    // 16-bit activation tiles are 256 bytes a row: only the 128x128 tile's
-    // three stages (123 KB) fit in LDS
+    // 16-bit activation tiles are 256 bytes a row: the 128x128 tile's three
+    // stages take 123 KB (one workgroup per CU).  With MXFP4 weights 64x128
+    // tiles (75 KB, two per CU) are faster (4096x1152x4608: 84 -> 76 us);
+    // with NVFP4 weights, whose dequantization is dearer, the taller tile
+    // amortizes it over twice the rows and is as fast.
     if (dp.g.cv_c > 0) return hipErrorInvalidValue;
     if (dp.g.K / BK > 32) return launch_cfg<AK, WK, 2, 2, true>(lr, dp, s);
-    return launch_cfg<AK, WK, 2, 2, false>(lr, dp, s);
+    if constexpr (WK == K_MX4) return launch_cfg<AK, WK, 1, 2, false>(lr, dp, s);
+    else return launch_cfg<AK, WK, 2, 2, false>(lr, dp, s);
   } else {
     if (dp.g.cv_c > 0) return launch_conv<AK, WK>(dp, s);
     return launch_tiles<AK, WK>(lr, dp, s);
