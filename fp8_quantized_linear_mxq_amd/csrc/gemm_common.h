@@ -169,8 +169,8 @@ __device__ __forceinline__ void epilogue(const GemmP& p, v16f acc[2][2], float a
       for (int q = 0; q < 16; ++q) {
         const int row = m0 + wm * 64 + i * 32 + 8 * (q >> 2) + 4 * half + (q & 3);
         if (row < p.M && col_ok[j])
-          p.out[(int64_t)row * p.ld_out + col_out[j]] =
-              (uint16_t)f32_to_bf16_bits(acc[i][j][q] + b);
+          __builtin_nontemporal_store((uint16_t)f32_to_bf16_bits(acc[i][j][q] + b),
+                                      &p.out[(int64_t)row * p.ld_out + col_out[j]]);
       }
     }
   }

