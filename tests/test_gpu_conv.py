@@ -117,6 +117,7 @@ CASES = [
     ("MXFP8", ("MXFP4",), 2, 12, 1, 256, 33, 6),                     # one image column
     ("MXFP8", ("INT4",), 1, 48, 48, 128, 2000, 7),                   # 288 INT4 tiles: wide grid
     ("MXFP8", ("INT4",), 1, 48, 48, 384, 2000, 8),                   # wide grid, 54 K-tiles: slabs
+    ("MXFP8", ("NVFP4", "INT4"), 5, 1, 1, 128, 40, 9),               # 1x1 images: centre tap only
 ]
 
 
