@@ -101,9 +101,11 @@ def test_gemm_errors():
 
 
 # Shapes that make the MXFP4 x MXFP4 route pick each of its workgroup tiles
-# (128x128, 256x192, 256x256, and the slab-accumulating 128x128 past K = 4096
-# with a half K-tile at the end), all with ragged M and N tails.
-MX_TILE_SHAPES = [(130, 250, 384), (2000, 2300, 256), (4000, 4000, 256), (96, 130, 4224)]
+# (64x64 below 128 tiles of 128x128, 128x128, 256x192, 256x256, and the
+# slab-accumulating 128x128 past K = 4096 with a half K-tile at the end), all
+# with ragged M and N tails.
+MX_TILE_SHAPES = [(130, 250, 384), (1500, 1400, 256), (2000, 2300, 256), (4000, 4000, 256),
+                  (96, 130, 4224)]
 
 
 @pytest.mark.parametrize("m,n,k", MX_TILE_SHAPES)
