@@ -9,13 +9,20 @@ steps cycle through enough independent buffer sets (activations, codes,
 weights, outputs) that the working set exceeds 512 MB, twice the 256 MB
 Infinity Cache, so every step reads from HBM.
 
-Prints one JSON line.  ``value`` is whole-step GEMM throughput (2 M N K per
-step / step time) in TFLOP/s.  ``roofline`` describes the dominant kernel
-(the GEMM): its launches over all buffer sets are captured in a HIP graph and
-replayed between HIP events on the replay stream, which gives the average
-launch duration without host launch gaps (the quantize kernel is timed the
-same way); ``cpu_baseline`` times the CPU oracle on a bounded sample of the
-same workload.
+Prints one JSON line.  ``value`` is whole-step GEMM throughput (the layer's
+GEMM work, 2 M N K plus 2 M N r for a rank-r branch, per step / step time) in
+TFLOP/s.  ``roofline`` describes the dominant kernel (the GEMM): its launches
+over all buffer sets are captured in a HIP graph and replayed between HIP
+events on the replay stream, which gives the average launch duration without
+host launch gaps (the quantize kernel is timed the same way).  Its peak is the
+route's: dense MXFP4 for MXFP4 x MXFP4, dense FP8 for an FP8 (MXFP8)
+activation operand against 4-bit weights, bf16 for NVFP4 and the 16-bit
+routes; the record also gives the fraction against the MFMA type the kernel
+actually issues.  ``cpu_baseline`` times the CPU oracle on a bounded sample of
+the same workload, on a pinned number of BLAS threads.
+
+Default workload: svdq_r32, the MXFP4 x MXFP4 layer (4096 x 3072 x 3072 with
+a rank-32 branch) on which the GEMM's MXFP4 roofline fraction is judged.
 """
 from __future__ import annotations
 
@@ -26,7 +33,23 @@ import os
 import sys
 import time
 
-import numpy as np
+
+def _host_threads() -> int:
+    """Threads the CPU oracle may use: the CPUs this process may run on,
+    capped at 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+# the oracle's BLAS thread count is pinned before numpy loads its BLAS
+BLAS_THREADS = _host_threads()
+for _v in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ[_v] = str(BLAS_THREADS)
+
+import numpy as np  # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -35,7 +58,7 @@ from fp8_quantized_linear_mxq_amd import workloads as wl  # noqa: E402
 
 PEAK_TFLOPS = {"mxfp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0, "fp16": 2500.0}
 HBM_GBPS = 8000.0
-DEFAULT_WORKLOAD = "w4a8_mlp"
+DEFAULT_WORKLOAD = "svdq_r32"
 CSRC = os.path.join(ROOT, "fp8_quantized_linear_mxq_amd", "csrc")
 
 
@@ -48,6 +71,7 @@ def kernel_source_digest() -> str:
 
 
 def gemm_dtype(act_fmt: str, w_fmt: str) -> str:
+    """The MFMA type the GEMM kernel issues for this pair."""
     if act_fmt == "MXFP4" and w_fmt == "MXFP4":
         return "mxfp4"
     if act_fmt == "NVFP4" and w_fmt == "NVFP4":
@@ -55,18 +79,36 @@ def gemm_dtype(act_fmt: str, w_fmt: str) -> str:
     return "bf16"
 
 
-def quantize_bytes(w: wl.Workload, cols: int | None = None) -> int:
-    """Algorithmic HBM bytes of one activation quantize: read x, write codes
-    and scales (and u for the low-rank branch).  ``cols``: the quantized
-    width when it is not K (the convolution's input channels)."""
+def route_peak_dtype(act_fmt: str, w_fmt: str) -> str:
+    """The peak each route is judged against: dense MXFP4 for MXFP4 x MXFP4,
+    dense FP8 for FP8 (MXFP8) activations against 4-bit MX / INT4 weights,
+    bf16 for NVFP4 operands and unquantized bf16 activations."""
+    if act_fmt == "MXFP4" and w_fmt == "MXFP4":
+        return "mxfp4"
+    if act_fmt == "MXFP8" and w_fmt in ("MXFP4", "INT4", "MIXED"):
+        return "fp8"
+    return "bf16"
+
+
+def gemm_flops(w) -> float:
+    """The layer's GEMM work: 2 M N K plus 2 M N r for the rank-r branch."""
+    return 2.0 * w.m * w.n * w.k + 2.0 * w.m * w.n * w.rank
+
+
+def quantize_bytes(w: wl.Workload, cols: int | None = None, rows: int | None = None) -> int:
+    """Algorithmic HBM bytes of one activation quantize: read x once, write
+    codes and scales (and u for the low-rank branch).  ``cols``/``rows``: the
+    quantized shape when it is not M x K (the convolution's input pixels).
+    NVFP4's dynamic tensor scale reads x a second time; that re-read is not
+    algorithmic (it can come from the Infinity Cache) and is reported as
+    measured traffic instead."""
     esz = 2 if w.act_dtype == "bf16" else 4
     k = w.k if cols is None else cols
-    rd = w.m * k * esz
-    code = w.m * k // (1 if w.act_fmt == "MXFP8" else 2)
-    scale = w.m * k // (16 if w.act_fmt == "NVFP4" else 32)
-    wr = code + scale + (w.m * w.rank * 4 if w.rank else 0)
-    if w.act_fmt == "NVFP4":
-        rd *= 2            # the dynamic tensor scale needs a first pass over x
+    m = w.m if rows is None else rows
+    rd = m * k * esz
+    code = m * k // (1 if w.act_fmt == "MXFP8" else 2)
+    scale = m * k // (16 if w.act_fmt == "NVFP4" else 32)
+    wr = code + scale + (m * w.rank * 4 if w.rank else 0)
     return rd + wr
 
 
@@ -191,30 +233,82 @@ def graph_avg_ms(torch, calls, min_launches: int) -> float:
     return e0.elapsed_time(e1) / (reps * len(calls))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
+    from threadpoolctl import threadpool_info
+    return max([t.get("num_threads", 1) for t in threadpool_info()
+                if t.get("user_api") == "blas"] + [1])
+
+
+def _oracle_conv_weights(w: wl.Workload):
+    """The convolution layer's weights as the oracle prepares them: per-row
+    format choice over {INT4, MXFP4, NVFP4} (one NVFP4 tensor scale over all
+    of W), each row quantized in its chosen format and dequantized; returns
+    float64 [N, K] in output-channel order and the rows per format."""
+    from oracle import quantize as oq
+    from oracle import select as osel
+
+    wt = wl.weights(w)
+    choice, _, _ = osel.select_formats(wt)
+    g = oq.nvfp4_tensor_scale(wt)
+    w_deq = np.empty(wt.shape, dtype=np.float64)
+    counts = []
+    for ci, fmt in enumerate(osel.PALETTE):
+        rows = np.nonzero(choice == ci)[0]
+        counts.append(int(rows.size))
+        if rows.size:
+            q = oq.quantize(wt[rows], fmt, tensor_scale=g if fmt == oq.NVFP4 else None)
+            w_deq[rows] = oq.dequantize(q)
+    return w_deq, counts
+
+
 def cpu_baseline(w: wl.Workload, budget_s: float = 12.0) -> dict:
     """The oracle, as it stands, on a bounded row sample of the workload:
     activation quantize + float64 GEMM (+ low-rank branch) per row, in chunks
     of growing size, passing over the (at most 4096) sampled rows again until
-    about budget_s seconds of CPU work are done."""
-    from threadpoolctl import threadpool_info
-
+    about budget_s seconds of CPU work are done.  For the convolution layer
+    the rows are the first output pixels' im2col rows (MXFP8) against the
+    mixed-format weights the oracle selects and quantizes beforehand (not
+    timed)."""
     from oracle import gemm as og
     from oracle import hadamard as oh
     from oracle import quantize as oq
     from oracle.formats import round_to_bf16
 
-    wt = wl.weights(w)
-    w_rot = oh.rotate(wt, w.hadamard, 7) if w.hadamard else wt
-    qw = oq.quantize(w_rot, w.w_fmt)
-    w_deq = oq.dequantize(qw)
+    conv = w.w_fmt == "MIXED"
+    prep = time.perf_counter()
+    if conv:
+        w_deq, counts = _oracle_conv_weights(w)
+        lh, lw, lc = w.extra["latent"]
+        lat_rows = 24                      # output image rows sampled
+        # their im2col rows read latent rows 0 .. lat_rows (one row below)
+        lat = wl.conv_latent(w)[:lat_rows + 1]
+        cols = wl.im2col(lat)[:lat_rows * lw]
+        vals = wl.bf16_to_f32(cols)
+        del lat, cols
+    else:
+        wt = wl.weights(w)
+        w_rot = oh.rotate(wt, w.hadamard, 7) if w.hadamard else wt
+        w_deq = oq.dequantize(oq.quantize(w_rot, w.w_fmt))
+        act = wl.activations(w, rows=min(w.m, 4096))
+        vals = wl.bf16_to_f32(act) if w.act_dtype == "bf16" else act
+    prep = time.perf_counter() - prep
     if w.rank:
         l1, l2 = wl.lowrank_factors(w)
         l1v = wl.bf16_to_f32(l1).astype(np.float64)
         l2v = wl.bf16_to_f32(l2).astype(np.float64)
-    rows = 64
+    rows = 64 if not conv else 16
     done_rows, elapsed, pos = 0, 0.0, 0
-    act = wl.activations(w, rows=min(w.m, 4096))
-    vals = wl.bf16_to_f32(act) if w.act_dtype == "bf16" else act
     while elapsed < budget_s:
         pos = 0 if pos >= vals.shape[0] else pos
         chunk = vals[pos:pos + rows]
@@ -228,17 +322,19 @@ def cpu_baseline(w: wl.Workload, budget_s: float = 12.0) -> dict:
         round_to_bf16(y)
         elapsed += time.perf_counter() - t0
         done_rows += chunk.shape[0]
-        rows = min(rows * 2, 1024)
-    flops = 2.0 * done_rows * w.n * w.k
-    threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+        rows = min(rows * 2, 1024 if not conv else 256)
+    flops = gemm_flops(w) * done_rows / w.m
+    what = (f"{w.act_fmt} quantize of im2col rows + float64 GEMM against the oracle's "
+            f"per-row formats (INT4/MXFP4/NVFP4 rows {counts[0]}/{counts[1]}/{counts[2]}; "
+            f"selection and weight quantization {prep:.1f} s, not timed)") if conv else (
+        f"{'bf16 activations' if w.act_fmt == 'BF16' else w.act_fmt + ' quantize'}"
+        f"{' + H' + str(w.hadamard) if w.hadamard else ''} + float64 GEMM "
+        f"against {w.w_fmt} weights{' + rank-' + str(w.rank) + ' branch' if w.rank else ''}")
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
             "kind": "oracle",
             "sample": f"{done_rows} rows ({done_rows / vals.shape[0]:.1f} passes over {vals.shape[0]} "
-                      f"of the {w.m} rows): oracle "
-                      f"{'bf16 activations' if w.act_fmt == 'BF16' else w.act_fmt + ' quantize'}"
-                      f"{' + H' + str(w.hadamard) if w.hadamard else ''} + float64 GEMM "
-                      f"against {w.w_fmt} weights{' + rank-' + str(w.rank) + ' branch' if w.rank else ''}"
-                      f", {elapsed:.1f} s"}
+                      f"of the {w.m} rows): oracle {what}, {elapsed:.1f} s",
+            "cpu_model": cpu_model(), "blas_threads_pinned": BLAS_THREADS}
 
 
 def main() -> int:
@@ -275,14 +371,23 @@ def main() -> int:
     if implicit:
         lat_h, lat_w, lat_c = w.extra["latent"]
     fa = wl_fmt(mxq, w.act_fmt)
+    if mixed:
+        # the activation format is read per step from the layer's table of
+        # ten timestep buckets (every bucket MXFP8 for this convolution)
+        act_table = wl.chameleon_act_table(1, mxq.MXFP8).reshape(-1)
+        num_steps = max(1, args.steps)
 
     bf16_act = w.act_fmt == "BF16"
 
-    def quant(s):
+    def quant(s, i=0):
         if bf16_act:
             return
         if mixed:
-            mxq.quantize(s["x"], fa, out=s["qa"])
+            f = mxq.act_format_for_step(act_table, 1, wl.ACT_TABLE_BUCKETS, 0, i % num_steps,
+                                        num_steps)
+            if f != s["qa"].fmt:
+                raise RuntimeError(f"table routes format {f}; the buffers hold {s['qa'].fmt}")
+            mxq.quantize(s["x"], f, out=s["qa"])
         else:
             mxq.quantize(s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], u=s["u"], out=s["qa"],
                          workspace=s["ws"])
@@ -297,17 +402,17 @@ def main() -> int:
         else:
             mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"], workspace=s["ws"])
 
-    def step(s):
-        quant(s)
+    def step(s, i):
+        quant(s, i)
         gemm(s)
 
     for i in range(args.warmup):
-        step(sets[i % n_sets])
+        step(sets[i % n_sets], i)
     torch.cuda.synchronize()
     # timed region: exactly `steps` steps, wall clock, synchronized both sides
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(sets[i % n_sets])
+        step(sets[i % n_sets], i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # per-kernel durations: each kernel's launches over all buffer sets are
@@ -341,10 +446,11 @@ def main() -> int:
         torch.cuda.synchronize()
 
     ms = wall / args.steps * 1e3
-    flops = 2.0 * w.m * w.n * w.k + (2.0 * w.m * w.n * 2 * w.rank if w.rank else 0.0)
+    flops = gemm_flops(w)
     gdt = gemm_dtype(w.act_fmt, w.w_fmt)
+    rdt = route_peak_dtype(w.act_fmt, w.w_fmt)
     achieved = flops / (g_ms * 1e-3) / 1e12
-    traffic = None
+    traffic = q2_fetch = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
         with open(tfile) as f:
@@ -352,10 +458,12 @@ def main() -> int:
         ent = t.get(w.name)
         if ent and ent.get("kernel_source_digest") == kernel_source_digest():
             traffic = ent.get("gemm_hbm_bytes_per_launch")
-    qbytes = None if bf16_act else quantize_bytes(w, lat_c if implicit else None)
+            q2_fetch = ent.get("quantize_second_pass_fetch_bytes")
+    qbytes = None if bf16_act else quantize_bytes(
+        w, lat_c if implicit else None, lat_h * lat_w if implicit else None)
     rec = {
         "metric": "block-scaled GEMM TFLOP/s & % MXFP4 peak; quantize GB/s & % HBM BW",
-        "value": round(2.0 * w.m * w.n * w.k / (ms * 1e-3) / 1e12, 2),
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -369,16 +477,20 @@ def main() -> int:
         "config": {"workload": w.name, "M": w.m, "K": w.k, "N": w.n,
                    "activations": f"{w.act_dtype} -> {w.act_fmt}", "weights": w.w_fmt,
                    "hadamard": w.hadamard, "lowrank": w.rank, "buffer_sets": n_sets,
-                   "working_set_MB": round(n_sets * per_set / 1e6, 1)},
+                   "working_set_MB": round(n_sets * per_set / 1e6, 1),
+                   "gemm_flops_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": PEAK_TFLOPS[gdt], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS[gdt], 4), "traffic": traffic,
-                     "kernel": "gemm", "avg_launch_us": round(g_ms * 1e3, 3)},
+                     "peak": PEAK_TFLOPS[rdt], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS[rdt], 4), "traffic": traffic,
+                     "kernel": "gemm", "avg_launch_us": round(g_ms * 1e3, 3),
+                     "route_peak_dtype": rdt, "mfma_dtype_issued": gdt,
+                     "frac_vs_issued_mfma_peak": round(achieved / PEAK_TFLOPS[gdt], 4)},
         "gemm_pct_mxfp4_peak": round(achieved / PEAK_TFLOPS["mxfp4"], 4),
         "quantize": None if bf16_act else {
             "avg_launch_us": round(q_ms * 1e3, 3), "algorithmic_bytes": qbytes,
             "GBps": round(qbytes / (q_ms * 1e-3) / 1e9, 1),
-            "frac_hbm": round(qbytes / (q_ms * 1e-3) / 1e9 / HBM_GBPS, 4)},
+            "frac_hbm": round(qbytes / (q_ms * 1e-3) / 1e9 / HBM_GBPS, 4),
+            "second_pass_fetch_bytes": q2_fetch if w.act_fmt == "NVFP4" else None},
         "kernel_source_digest": kernel_source_digest(),
     }
     if mixed:
@@ -389,7 +501,7 @@ def main() -> int:
         rec["config"]["conv"] = ("implicit im2col: quantize the 128x128x2560 input once, "
                                  "gather the 3x3 taps in the GEMM") if implicit else \
             "explicit im2col: quantize the 16384x23040 matrix"
-    if not args.no_cpu_baseline and not mixed:
+    if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(rec), flush=True)
     return 0
