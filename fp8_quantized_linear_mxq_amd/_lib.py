@@ -23,7 +23,7 @@ BLOCK = {MXFP4: 32, MXFP8: 32, NVFP4: 16, INT4: 32}
 
 STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARG", 2: "MXQ_ERR_UNSUPPORTED",
           3: "MXQ_ERR_ALIGNMENT", 4: "MXQ_ERR_SHAPE", 5: "MXQ_ERR_WORKSPACE",
-          6: "MXQ_ERR_NO_DEVICE", 7: "MXQ_ERR_LAUNCH"}
+          6: "MXQ_ERR_NO_DEVICE", 7: "MXQ_ERR_LAUNCH", 8: "MXQ_ERR_NONFINITE"}
 
 # Every symbol include/mxq.h declares.
 EXPORTS = ("mxq_quantize", "mxq_gemm", "mxq_gemm_mixed", "mxq_conv3x3_gemm_mixed",

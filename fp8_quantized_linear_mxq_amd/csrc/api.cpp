@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "kernels.h"
@@ -61,6 +62,37 @@ mxq_status check_qtensor(const mxq_qtensor* t) {
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// MXQ_DEBUG_CHECKS=1 in the environment (read at every call) turns on the
+// device-side NaN / Inf checks of the quantize and format-choice kernels.
+bool debug_checks() {
+  const char* e = std::getenv("MXQ_DEBUG_CHECKS");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+// Run once a call has passed validation and is about to enqueue work: a
+// usable device, and in debug mode the non-finite flag a previous call may
+// have set (read and cleared synchronously).  *dbg receives the flag's
+// device address for the kernels (null outside debug mode).
+mxq_status device_entry(unsigned** dbg) {
+  *dbg = nullptr;
+  int dev = -1, count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0 || hipGetDevice(&dev) != hipSuccess)
+    return MXQ_ERR_NO_DEVICE;
+  if (!debug_checks()) return MXQ_OK;
+  unsigned* flag = nullptr;
+  if (nonfinite_flag_ptr(&flag) != hipSuccess) return MXQ_ERR_LAUNCH;
+  unsigned v = 0;
+  if (hipMemcpy(&v, flag, sizeof v, hipMemcpyDeviceToHost) != hipSuccess) return MXQ_ERR_LAUNCH;
+  if (v != 0) {
+    const unsigned zero = 0;
+    if (hipMemcpy(flag, &zero, sizeof zero, hipMemcpyHostToDevice) != hipSuccess)
+      return MXQ_ERR_LAUNCH;
+    return MXQ_ERR_NONFINITE;
+  }
+  *dbg = flag;
+  return MXQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,6 +109,7 @@ const char* mxq_status_string(int32_t status) {
     case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
     case MXQ_ERR_NO_DEVICE: return "no HIP device";
     case MXQ_ERR_LAUNCH: return "kernel launch failed";
+    case MXQ_ERR_NONFINITE: return "NaN or Inf input seen by an earlier call (debug checks)";
     default: return "unknown status";
   }
 }
@@ -118,10 +151,14 @@ int32_t mxq_act_format_for_step(const uint8_t* table, int32_t n_layers, int32_t 
   return table[(int64_t)layer * n_buckets + bucket];
 }
 
-mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ldx,
-                        int32_t hadamard_n, const float* static_tensor_scale,
-                        const void* lr_l1t, int32_t lr_rank, float* lr_u, int64_t ld_u,
-                        mxq_qtensor* out, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// mxq_quantize.
+static mxq_status quantize_impl(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                int64_t ldx, int32_t hadamard_n,
+                                const float* static_tensor_scale, const void* lr_l1t,
+                                int32_t lr_rank, float* lr_u, int64_t ld_u, mxq_qtensor* out,
+                                void* workspace, size_t ws_bytes, void* stream) {
   if (!out || (dtype != MXQ_DT_F32 && dtype != MXQ_DT_BF16) || rows < 0 || cols < 0)
     return MXQ_ERR_INVALID_ARG;
   if (!known_fmt(out->fmt) || out->rows != rows || out->cols != cols) return MXQ_ERR_INVALID_ARG;
@@ -143,6 +180,9 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
   }
   const bool dynamic_nv = out->fmt == MXQ_FMT_NVFP4 && !static_tensor_scale;
   if (dynamic_nv && (!workspace || ws_bytes < (size_t)kAmaxPartials * 4)) return MXQ_ERR_WORKSPACE;
+  unsigned* dbg = nullptr;
+  st = device_entry(&dbg);
+  if (st != MXQ_OK) return st;
 
   QuantizeArgs a;
   a.x = x;
@@ -159,6 +199,7 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
   a.tensor_scale_out = out->tensor_scale;
   a.static_tensor_scale = static_tensor_scale;
   a.partials = static_cast<float*>(workspace);
+  a.dbg = dbg;
   LoraDownArgs l;
   a.lr = nullptr;
   if (lr_rank > 0) {
@@ -175,6 +216,17 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
   hipError_t e = launch_quantize(a, as_stream(stream));
   return from_hip(e);
 }
+
+extern "C" {
+
+mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                        int32_t hadamard_n, const float* static_tensor_scale,
+                        const void* lr_l1t, int32_t lr_rank, float* lr_u, int64_t ld_u,
+                        mxq_qtensor* out, void* workspace, size_t ws_bytes, void* stream) {
+  return quantize_impl(x, dtype, rows, cols, ldx, hadamard_n, static_tensor_scale, lr_l1t,
+                       lr_rank, lr_u, ld_u, out, workspace, ws_bytes, stream);
+}
+
 
 static mxq_status gemm_checks(const mxq_qtensor* a, const mxq_qtensor* w, const float* lr_u,
                               int64_t ld_u, const void* lr_l2t, int32_t lr_rank, void* out,
@@ -256,6 +308,9 @@ mxq_status mxq_gemm(const mxq_qtensor* a, const mxq_qtensor* w, const int32_t* w
   if (workspace && !aligned(workspace, 16)) return MXQ_ERR_ALIGNMENT;
   if (a->rows == 0 || w->rows == 0 || n_out == 0) return MXQ_OK;
   if (!w_out_col && w->rows > n_out) return MXQ_ERR_SHAPE;
+  unsigned* dbg = nullptr;
+  st = device_entry(&dbg);
+  if (st != MXQ_OK) return st;
   return from_hip(gemm_launch(a, w, w_out_col, lr_u, ld_u, lr_l2t, lr_rank, bias, out, ld_out,
                               n_out, workspace, ws_bytes, as_stream(stream)));
 }
@@ -275,6 +330,9 @@ mxq_status mxq_gemm_mixed(const mxq_qtensor* a, const mxq_qtensor* w_groups, int
   }
   if (total > 0 && !w_perm) return MXQ_ERR_INVALID_ARG;
   if (a->rows == 0 || n_out == 0) return MXQ_OK;
+  unsigned* dbg = nullptr;
+  const mxq_status dst = device_entry(&dbg);
+  if (dst != MXQ_OK) return dst;
   int64_t off = 0;
   for (int g = 0; g < n_groups; ++g) {
     const mxq_qtensor* w = &w_groups[g];
@@ -323,6 +381,9 @@ mxq_status mxq_conv3x3_gemm_mixed(const mxq_qtensor* x, int64_t height, int64_t 
   if (!aligned(out, 2)) return MXQ_ERR_ALIGNMENT;
   // without a permutation a single group's row j is output column j
   if (!w_perm && (n_groups > 1 || total > n_out)) return MXQ_ERR_INVALID_ARG;
+  unsigned* dbg = nullptr;
+  st = device_entry(&dbg);
+  if (st != MXQ_OK) return st;
   int64_t off = 0;
   for (int g = 0; g < n_groups; ++g) {
     const mxq_qtensor* w = &w_groups[g];
@@ -355,7 +416,11 @@ mxq_status mxq_select_format(const void* w, int32_t dtype, int64_t n, int64_t k,
   if (!aligned(w, 16) || (ldw * esz) % 16) return MXQ_ERR_ALIGNMENT;
   const int64_t need = mxq_workspace_size(MXQ_OP_SELECT, n, k, 0);
   if (!workspace || ws_bytes < (size_t)need || !aligned(workspace, 16)) return MXQ_ERR_WORKSPACE;
+  unsigned* dbg = nullptr;
+  const mxq_status dst = device_entry(&dbg);
+  if (dst != MXQ_OK) return dst;
   SelectArgs a;
+  a.dbg = dbg;
   a.w = w;
   a.dtype = dtype;
   a.n = n;

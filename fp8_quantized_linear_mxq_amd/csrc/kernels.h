@@ -30,11 +30,16 @@ struct QuantizeArgs {
   const float* static_tensor_scale; // NVFP4, may be null
   float* partials;                  // NVFP4 dynamic: workspace
   const LoraDownArgs* lr;           // optional low-rank down projection (bf16 x)
+  unsigned* dbg;                    // debug checks: non-finite flag, else null
 };
 
 constexpr int kAmaxPartials = 1024;  // NVFP4 phase-1 grid (workspace floats)
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s);
+
+// Device address of the non-finite input flag of the current device (the
+// debug checks): kernels given it set it to 1 when an input is NaN or Inf.
+hipError_t nonfinite_flag_ptr(unsigned** out);
 
 
 
@@ -74,6 +79,7 @@ struct SelectArgs {
   float* partials;   // workspace: kAmaxPartials floats
   double* sse_ws;    // workspace: n * n_cand doubles (when sse is null)
   float* g_ws;       // workspace: one float
+  unsigned* dbg;     // debug checks: non-finite flag, else null
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 

@@ -13,6 +13,8 @@
 // maxima) are in-lane; the 16/32-point Hadamard butterflies run in float64
 // registers in-lane (128 points: two more stages across the block's 4 lanes);
 // a lane's codes leave as one 16-byte (FP4/INT4) or 32-byte (FP8) store.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -34,7 +36,23 @@ struct QParams {
   const float* g_static;
   const float* partials;
   int n_partials;
+  unsigned* dbg;    // MXQ_DEBUG_CHECKS: set to 1 on a NaN / Inf input, else null
 };
+
+// One flag per device for the debug checks (NaN / Inf inputs); the host
+// reads and clears it through its symbol address.
+__device__ unsigned int g_nonfinite;
+
+// Flags the device when any of a lane's loaded values is NaN or Inf (only
+// with the debug checks on: dbg is null otherwise).
+template <int N>
+__device__ __forceinline__ void check_finite(const float* v, unsigned* dbg) {
+  if (!dbg) return;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < N; ++i) bad |= !__builtin_isfinite(v[i]);
+  if (bad) atomicOr(dbg, 1u);
+}
 
 template <int HAD>
 __device__ constexpr double had_scale() {
@@ -351,6 +369,7 @@ __global__ __launch_bounds__(kThreads) void quantize32_kernel(QParams p, uint32_
     const int64_t row = bb / bpr, col = (int64_t)(bb - (uint32_t)row * bpr) * 32;
     float v[4][8];
     load32<DT>(p, row, col, v);
+    check_finite<32>(&v[0][0], p.dbg);
     if constexpr (HAD > 0) hadamard32<HAD>(v, lane);
     uint32_t code[4][8], sbyte[4];
     float sfloat[4];
@@ -372,6 +391,7 @@ __global__ __launch_bounds__(kThreads) void amax32_kernel(QParams p, float* part
     const int64_t row = bb / bpr, col = (int64_t)(bb - (uint32_t)row * bpr) * 32;
     float v[4][8];
     load32<DT>(p, row, col, v);
+    check_finite<32>(&v[0][0], p.dbg);
     if constexpr (HAD > 0) hadamard32<HAD>(v, lane);
     if (act) {
 #pragma unroll
@@ -451,6 +471,7 @@ __global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, L
           v[j][2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
         }
       }
+      check_finite<32>(&v[0][0], p.dbg);
       float m[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -576,6 +597,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelParams sp) {
     const bool act = c < p.cpr;
     float v[8];
     load_chunk<DT>(p, row, act ? c * 8u : 0u, act, v);
+    check_finite<8>(v, p.dbg);
     float m = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
@@ -707,6 +729,26 @@ hipError_t dispatch_amax(int had, dim3 grid, const QParams& p, float* partials, 
 
 }  // namespace
 
+hipError_t nonfinite_flag_ptr(unsigned** out) {
+  // the flag's address on the current device, looked up once per device
+  constexpr int kMaxDev = 64;
+  static std::atomic<unsigned*> cache[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  unsigned* flag = cache[dev].load(std::memory_order_acquire);
+  if (!flag) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_nonfinite));
+    if (e != hipSuccess) return e;
+    flag = static_cast<unsigned*>(ptr);
+    cache[dev].store(flag, std::memory_order_release);
+  }
+  *out = flag;
+  return hipSuccess;
+}
+
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   QParams p;
   p.x = a.x;
@@ -721,6 +763,7 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   p.g_static = a.static_tensor_scale;
   p.partials = a.partials;
   p.n_partials = 0;
+  p.dbg = a.dbg;
 
   // one lane per 32-block
   const uint32_t bpr = (uint32_t)(a.cols / 32);
@@ -774,6 +817,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   p.g_out = a.g_out ? a.g_out : a.g_ws;
   p.g_static = nullptr;
   p.partials = a.partials;
+  p.dbg = a.dbg;
   if (a.n == 0) return hipSuccess;
   const uint32_t bpr = (uint32_t)(a.k / 32), nblk = (uint32_t)(a.n * bpr);
   uint32_t blocks = (nblk + kThreads - 1) / kThreads;

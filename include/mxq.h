@@ -53,11 +53,21 @@
  *  - Streams: work is enqueued on `stream` (a hipStream_t passed as void*;
  *    NULL is the default stream) and the call returns without waiting.
  *  - Errors: invalid arguments are reported synchronously, before any work
- *    is enqueued, as an mxq_status; a failed launch returns MXQ_ERR_LAUNCH.
- *    Faults inside kernels surface at the caller's next synchronization.
- *    No C++ exception crosses this interface.
- *  - NaN or Inf inputs are outside the contract.
- *  - The library keeps no state; calls on distinct streams are independent.
+ *    is enqueued, as an mxq_status; a call that would enqueue work returns
+ *    MXQ_ERR_NO_DEVICE when no HIP device is available (checked after the
+ *    arguments); a failed launch returns MXQ_ERR_LAUNCH.  Faults inside
+ *    kernels surface at the caller's next synchronization.  No C++
+ *    exception crosses this interface.
+ *  - NaN or Inf inputs are outside the contract: results are unspecified
+ *    (every code and scale written stays a valid bit pattern and no memory
+ *    outside the outputs is touched).  With MXQ_DEBUG_CHECKS=1 in the
+ *    environment (read at every call), mxq_quantize and mxq_select_format
+ *    flag such inputs on the device, and the next call that enqueues work
+ *    on that device returns MXQ_ERR_NONFINITE (and clears the flag) instead
+ *    of running.  Debug mode reads the flag synchronously at every such
+ *    call, so it synchronizes the device and cannot be graph-captured.
+ *  - Apart from that one debug flag per device the library keeps no state;
+ *    calls on distinct streams are independent.
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -79,7 +89,8 @@ typedef enum mxq_status {
   MXQ_ERR_SHAPE = 4,       /* K not a multiple of the block / tile / rotation*/
   MXQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required     */
   MXQ_ERR_NO_DEVICE = 6,   /* no HIP device available                        */
-  MXQ_ERR_LAUNCH = 7       /* kernel launch failed                           */
+  MXQ_ERR_LAUNCH = 7,      /* kernel launch failed                           */
+  MXQ_ERR_NONFINITE = 8    /* debug checks: an earlier call saw NaN / Inf    */
 } mxq_status;
 
 typedef enum mxq_format {

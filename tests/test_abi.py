@@ -129,3 +129,23 @@ def test_validation_before_device_work(lib):
     cand = (C.c_int32 * 1)(1)
     assert lib.mxq_select_format(vp(16), 1, 4, 48, 48, cand, 1, vp(64), None, None, None, None,
                                  None, 0, None) == 4
+
+
+def test_status_codes_and_no_device(lib):
+    assert lib.mxq_status_string(8).startswith(b"NaN or Inf")
+    assert _lib.STATUS[8] == "MXQ_ERR_NONFINITE"
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call below would enqueue work")
+    # valid arguments with aligned stand-in pointers that are never
+    # dereferenced: validation passes and the call stops at the device check
+    vp = C.c_void_p
+    q = _lib.QTensorC(1, 0, 4, 64, 1 << 20, 32, 1 << 21, 4, None)
+    st = lib.mxq_quantize(vp(1 << 22), 1, 4, 64, 64, 0, None, None, 0, None, 0, C.byref(q),
+                          None, 0, None)
+    assert st == 6
+    w = _lib.QTensorC(1, 0, 8, 128, 1 << 23, 64, 1 << 24, 4, None)
+    a = _lib.QTensorC(1, 0, 4, 128, 1 << 25, 64, 1 << 26, 4, None)
+    st = lib.mxq_gemm(C.byref(a), C.byref(w), None, None, 0, None, 0, None, vp(1 << 27), 8, 8,
+                      None, 0, None)
+    assert st == 6
