@@ -26,7 +26,7 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARG", 2: "MXQ_ERR_UNSUPPORTED",
           6: "MXQ_ERR_NO_DEVICE", 7: "MXQ_ERR_LAUNCH", 8: "MXQ_ERR_NONFINITE"}
 
 # Every symbol include/mxq.h declares.
-EXPORTS = ("mxq_quantize", "mxq_gemm", "mxq_gemm_mixed", "mxq_conv3x3_gemm_mixed",
+EXPORTS = ("mxq_quantize", "mxq_quantize_noalloc", "mxq_gemm", "mxq_gemm_mixed", "mxq_conv3x3_gemm_mixed",
            "mxq_select_format",
            "mxq_act_format_for_step", "mxq_workspace_size", "mxq_storage",
            "mxq_status_string", "mxq_version")
@@ -66,6 +66,8 @@ def load():
     qp = C.POINTER(QTensorC)
     lib.mxq_quantize.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i32, vp, i64, qp, vp, sz, vp]
     lib.mxq_quantize.restype = i32
+    lib.mxq_quantize_noalloc.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i32, vp, i64, qp, vp]
+    lib.mxq_quantize_noalloc.restype = i32
     lib.mxq_gemm.argtypes = [qp, qp, vp, vp, i64, vp, i32, vp, vp, i64, i64, vp, sz, vp]
     lib.mxq_gemm.restype = i32
     lib.mxq_gemm_mixed.argtypes = [qp, qp, i32, vp, vp, i64, vp, i32, vp, vp, i64, i64, vp, sz, vp]

@@ -153,12 +153,14 @@ int32_t mxq_act_format_for_step(const uint8_t* table, int32_t n_layers, int32_t 
 
 }  // extern "C"
 
-// mxq_quantize.
+// mxq_quantize and its allocation-free variant: with `noalloc` the NVFP4
+// amax partials go to the library's per-device scratch array instead of a
+// caller workspace.
 static mxq_status quantize_impl(const void* x, int32_t dtype, int64_t rows, int64_t cols,
                                 int64_t ldx, int32_t hadamard_n,
                                 const float* static_tensor_scale, const void* lr_l1t,
                                 int32_t lr_rank, float* lr_u, int64_t ld_u, mxq_qtensor* out,
-                                void* workspace, size_t ws_bytes, void* stream) {
+                                void* workspace, size_t ws_bytes, bool noalloc, void* stream) {
   if (!out || (dtype != MXQ_DT_F32 && dtype != MXQ_DT_BF16) || rows < 0 || cols < 0)
     return MXQ_ERR_INVALID_ARG;
   if (!known_fmt(out->fmt) || out->rows != rows || out->cols != cols) return MXQ_ERR_INVALID_ARG;
@@ -179,10 +181,19 @@ static mxq_status quantize_impl(const void* x, int32_t dtype, int64_t rows, int6
     if (!aligned(lr_l1t, 16) || !aligned(lr_u, 16) || ld_u % 4) return MXQ_ERR_ALIGNMENT;
   }
   const bool dynamic_nv = out->fmt == MXQ_FMT_NVFP4 && !static_tensor_scale;
-  if (dynamic_nv && (!workspace || ws_bytes < (size_t)kAmaxPartials * 4)) return MXQ_ERR_WORKSPACE;
+  if (!noalloc && dynamic_nv && (!workspace || ws_bytes < (size_t)kAmaxPartials * 4))
+    return MXQ_ERR_WORKSPACE;
   unsigned* dbg = nullptr;
   st = device_entry(&dbg);
   if (st != MXQ_OK) return st;
+  if (noalloc) {
+    // the partials never outgrow the scratch: one per amax workgroup, at
+    // most kAmaxPartials whatever the input size
+    size_t bytes = 0;
+    if (quantize_scratch(&workspace, &bytes) != hipSuccess) return MXQ_ERR_LAUNCH;
+    if (bytes < (size_t)kAmaxPartials * 4) return MXQ_ERR_WORKSPACE;
+    ws_bytes = bytes;
+  }
 
   QuantizeArgs a;
   a.x = x;
@@ -224,9 +235,17 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
                         const void* lr_l1t, int32_t lr_rank, float* lr_u, int64_t ld_u,
                         mxq_qtensor* out, void* workspace, size_t ws_bytes, void* stream) {
   return quantize_impl(x, dtype, rows, cols, ldx, hadamard_n, static_tensor_scale, lr_l1t,
-                       lr_rank, lr_u, ld_u, out, workspace, ws_bytes, stream);
+                       lr_rank, lr_u, ld_u, out, workspace, ws_bytes, false, stream);
 }
 
+mxq_status mxq_quantize_noalloc(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                int64_t ldx, int32_t hadamard_n,
+                                const float* static_tensor_scale, const void* lr_l1t,
+                                int32_t lr_rank, float* lr_u, int64_t ld_u, mxq_qtensor* out,
+                                void* stream) {
+  return quantize_impl(x, dtype, rows, cols, ldx, hadamard_n, static_tensor_scale, lr_l1t,
+                       lr_rank, lr_u, ld_u, out, nullptr, 0, true, stream);
+}
 
 static mxq_status gemm_checks(const mxq_qtensor* a, const mxq_qtensor* w, const float* lr_u,
                               int64_t ld_u, const void* lr_l2t, int32_t lr_rank, void* out,

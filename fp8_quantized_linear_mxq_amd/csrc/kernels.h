@@ -37,6 +37,10 @@ constexpr int kAmaxPartials = 1024;  // NVFP4 phase-1 grid (workspace floats)
 
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s);
 
+// Device address and size of the current device's scratch array for the
+// allocation-free quantize (the NVFP4 amax partials).
+hipError_t quantize_scratch(void** out, size_t* bytes);
+
 // Device address of the non-finite input flag of the current device (the
 // debug checks): kernels given it set it to 1 when an input is NaN or Inf.
 hipError_t nonfinite_flag_ptr(unsigned** out);

@@ -729,6 +729,31 @@ hipError_t dispatch_amax(int had, dim3 grid, const QParams& p, float* partials, 
 
 }  // namespace
 
+// Scratch of the allocation-free quantize entry point: room for the NVFP4
+// tensor-amax partials (one float per amax workgroup, at most kAmaxPartials)
+// on each device, held until the process ends.  Only its device address,
+// looked up once per device, is ever passed to a kernel.
+static __device__ __align__(256) float scratch[kAmaxPartials];
+
+hipError_t quantize_scratch(void** out, size_t* bytes) {
+  constexpr int kMaxDev = 64;
+  static std::atomic<void*> cache[kMaxDev];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  void* ptr = cache[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    // with this device current: its own copy of the array
+    e = hipGetSymbolAddress((void**)&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    cache[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  *bytes = sizeof(scratch);
+  return hipSuccess;
+}
+
 hipError_t nonfinite_flag_ptr(unsigned** out) {
   // the flag's address on the current device, looked up once per device
   constexpr int kMaxDev = 64;

@@ -162,6 +162,26 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
                         void* stream);
 
 /*
+ * mxq_quantize_noalloc -- mxq_quantize with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * results and errors as mxq_quantize; the scratch the dynamic NVFP4 tensor
+ * scale needs (its amax partials, at most 1024 floats whatever the input
+ * size, so no input is too large for it) lives in a 4 KB array of the
+ * library's own, one per device, held until the process ends.  The library
+ * looks up that array's address on the first call on each device (that call
+ * must run with the device current); nothing is allocated or freed, here or
+ * later.  Calls on one device share the array: calls that overlap in time on
+ * one device (different streams, no ordering between them) race and may
+ * produce wrong NVFP4 tensor scales; calls ordered on one stream do not.
+ */
+mxq_status mxq_quantize_noalloc(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                                int64_t ldx, int32_t hadamard_n,
+                                const float* static_tensor_scale,
+                                const void* lr_l1t, int32_t lr_rank, float* lr_u, int64_t ld_u,
+                                mxq_qtensor* out, void* stream);
+
+/*
  * mxq_gemm -- y = RN_bf16(alpha * Q(a) Q(w)^T + u L2 + bias) for one weight
  * format (Nunchaku article, main explanation: 4-bit GEMM plus the 16-bit
  * low-rank branch added in the same output).
