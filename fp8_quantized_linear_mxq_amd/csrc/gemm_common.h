@@ -183,11 +183,13 @@ namespace {
 // thread per output element.  (A copy per translation unit.)
 __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* part, int splits,
                                                                int M, int N, const float* a_gp,
+                                                               float pow2,
                                                                const int32_t* col_map,
                                                                const uint16_t* bias,
                                                                uint16_t* out, int64_t ld_out,
                                                                int n_out) {
-  const float alpha = a_gp ? *a_gp : 1.0f;
+  // pow2: the power of two undoing the activations' dequantization bias
+  const float alpha = a_gp ? pow2 * *a_gp : pow2;
   const int64_t total = (int64_t)M * N;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
@@ -202,11 +204,11 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(const float* pa
 }
 
 inline hipError_t launch_splitk_reduce(const GemmP& g, const float* part, int splits,
-                                       const float* alpha, hipStream_t s) {
+                                       const float* alpha, float pow2, hipStream_t s) {
   const int64_t total = (int64_t)g.M * g.N;
   const int64_t want = (total + kThreads - 1) / kThreads;
   const int blocks = (int)(want < 4096 ? want : 4096);
-  splitk_reduce_kernel<<<blocks, kThreads, 0, s>>>(part, splits, g.M, g.N, alpha, g.col_map,
+  splitk_reduce_kernel<<<blocks, kThreads, 0, s>>>(part, splits, g.M, g.N, alpha, pow2, g.col_map,
                                                    g.bias, g.out, g.ld_out, g.n_out);
   return hipGetLastError();
 }

@@ -13,6 +13,8 @@
 // Tile 128x128, K-tile 64, 2x2 waves of 64x64, 32x32x16 MFMAs; operands are
 // dequantized while being stored to LDS, so each element is converted once
 // per workgroup rather than once per wave.
+#include <cmath>
+
 #include "device_common.h"
 #include "gemm_common.h"
 #include "kernels.h"
@@ -123,8 +125,17 @@ __device__ __forceinline__ void dq_fp8_mx(const uint4& c, float sc, uint4 out[2]
   out[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Exponent bias of an MX activation operand: a block with E8M0 code c is
+// dequantized with the fp32 scale 2**(c - 127 + B), a normal float for every
+// code, so every dequantized value is a normal bf16 (B = 10 for MXFP8, whose
+// values reach down to 2**-9, 2 for MXFP4); the epilogue multiplies by 2**-B,
+// exactly.  MXFP8 blocks then need c <= 236 (amax below 2**117), MXFP4 blocks
+// c <= 250 (amax below 2**126).
+template <int K> constexpr int mx_bias() { return K == K_MX8 ? 10 : K == K_MX4 ? 2 : 0; }
+
+template <int K>
 __device__ __forceinline__ float e8m0_f32(uint32_t code) {
-  return code == 0 ? 0x1p-127f : __uint_as_float(code << 23);
+  return __uint_as_float((code + (uint32_t)mx_bias<K>()) << 23);
 }
 
 // A thread's staged 4-bit chunk of one K-tile: 32 codes and their scales.
@@ -171,7 +182,7 @@ struct Fp4Loader {
       dq_fp4_nv<FP16>(d.r, e4m3_value((d.s >> (16 * fc)) & 0xFFu),
                       e4m3_value((d.s >> (16 * fc + 8)) & 0xFFu), o);
     } else if constexpr (KIND == K_MX4) {
-      dq_fp4_mx(d.r, e8m0_f32(d.s), o);
+      dq_fp4_mx(d.r, e8m0_f32<K_MX4>(d.s), o);
     } else {
       dq_int4(d.r, o);
     }
@@ -317,7 +328,7 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         uint4 o2[2];
-        dq_fp8_mx(S.a16[i], e8m0_f32(S.a8s[i]), o2);
+        dq_fp8_mx(S.a16[i], e8m0_f32<K_MX8>(S.a8s[i]), o2);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           const int c = ac8[i] * 2 + k;
@@ -480,7 +491,8 @@ __device__ __forceinline__ void dq_body(const DqParams& dp) {
     }
     return;
   }
-  float alpha = 1.0f;
+  // undo the MX exponent bias (a power of two), then the NVFP4 tensor scales
+  float alpha = __uint_as_float((uint32_t)(127 - mx_bias<AK>()) << 23);
   if constexpr (AK == K_NV) alpha *= *dp.a_gp;
   if constexpr (WK == K_NV) alpha *= *dp.w_gp;
   epilogue<LR>(p, acc, alpha, m0, n0, wm, wn, lane);
@@ -533,7 +545,8 @@ hipError_t dispatch(bool lr, dim3 grid, const DqParams& p, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !p.part) return e;
-  return launch_splitk_reduce(p.g, p.part, (int)grid.y, AK == K_NV ? p.a_gp : nullptr, s);
+  return launch_splitk_reduce(p.g, p.part, (int)grid.y, AK == K_NV ? p.a_gp : nullptr,
+                              std::ldexp(1.0f, -mx_bias<AK>()), s);
 }
 
 template <int AK>

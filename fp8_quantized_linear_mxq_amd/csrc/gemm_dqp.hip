@@ -61,10 +61,20 @@ __device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
+// Exponent bias of an MX operand in this route: a block with E8M0 code c is
+// dequantized with the fp32 scale 2**(c - 127 + B), so that every code gives
+// a normal fp32 scale (2**-127 is a subnormal the converts do not apply
+// exactly) and every dequantized value is a normal bf16 (E4M3 values reach
+// down to 2**-9, E2M1 to 2**-1): B = 10 for MXFP8, 2 for MXFP4.  The
+// epilogue multiplies by 2**-(B_a + B_w), exactly.  The price is the top
+// codes: a value must stay below bf16's 2**128, so MXFP8 blocks need
+// c <= 236 (block amax below 2**117) and MXFP4 blocks c <= 250 (amax below
+// 2**126).
+template <int K> constexpr int mx_bias() { return K == K_MX8 ? 10 : K == K_MX4 ? 2 : 0; }
+
+template <int K>
 __device__ __forceinline__ float e8m0_scale(uint32_t code) {
-  // E8M0 as an fp32 power of two for the hardware converts; code 0 (2**-127,
-  // an fp32 subnormal the converts do not apply exactly) is taken as 2**-126
-  return __uint_as_float((code == 0 ? 1u : code) << 23);
+  return __uint_as_float((code + (uint32_t)mx_bias<K>()) << 23);
 }
 
 // The lane's block scales of a K-tile, one value per group of MFMA steps:
@@ -86,8 +96,8 @@ __device__ __forceinline__ Scales<K, FP16> lane_scales(uint32_t dw, int half) {
   } else {
     // bytes 2h, 2h+1 of the row's 4 scale bytes: 32-blocks 2h, 2h+1
     const uint32_t b = dw >> (16 * half);
-    r.s[0] = e8m0_scale(b & 0xFFu);
-    r.s[1] = e8m0_scale((b >> 8) & 0xFFu);
+    r.s[0] = e8m0_scale<K>(b & 0xFFu);
+    r.s[1] = e8m0_scale<K>((b >> 8) & 0xFFu);
   }
   return r;
 }
@@ -390,7 +400,8 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] += tot[i][j];
   }
-  float alpha = 1.0f;
+  // undo the MX exponent biases (a power of two), then the NVFP4 tensor scales
+  float alpha = __uint_as_float((uint32_t)(127 - mx_bias<AK>() - mx_bias<WK>()) << 23);
   if constexpr (AK == K_NV) alpha *= *dp.a_gp;
   if constexpr (WK == K_NV) alpha *= *dp.w_gp;
   wait_lgkmcnt0();

@@ -192,6 +192,16 @@ mxq_status mxq_quantize_noalloc(const void* x, int32_t dtype, int64_t rows, int6
  *              is supported: MXFP4 x MXFP4 on the scaled MFMA; the others
  *              dequantize exactly to fp16 (NVFP4 x NVFP4) or bf16 operands;
  *              INT4 rows sum each 32-block and apply its fp32 scale.
+ *              Input domain of the dequantizing routes (every pair except
+ *              MXFP4 x MXFP4): an MX operand's values are formed with its
+ *              exponent raised by 10 (MXFP8) or 2 (MXFP4), undone exactly
+ *              in the epilogue, so every E8M0 code down to 0 (2**-127)
+ *              dequantizes exactly; in exchange MXFP8 blocks must have scale
+ *              codes <= 236 (block amax below 2**117) and MXFP4 blocks codes
+ *              <= 250 (amax below 2**126).
+ * Error bound: |y - y_exact| <= 1e-5 (1 + 2**-8) S + 2**-8 |y_exact| + 2**-133
+ * with S = alpha sum_k |a w| + sum_j |u_j L2_jn| (the last two terms are the
+ * bf16 output rounding, 2**-133 covering subnormal outputs).
  *  alpha       the product of the NVFP4 tensor scales of a and w that are
  *              NVFP4 (read from their tensor_scale pointers on the device).
  *  w_out_col   optional device int32[N]: weight row n writes output column

@@ -210,3 +210,47 @@ def test_int4_wide_grid_lowrank(fa, k):
     w_deq = np.hstack([gu.dequant_w_for_gemm(qw), l2.T.astype(np.float64) / alpha])
     ratio = gu.check_gemm(y, a_deq, w_deq, alpha, bias=bias, rows=rows, tag=f"{fa}xINT4 wide")
     gu.say(f"  worst err/tol {ratio:.3g}")
+
+
+def _tiny_operands(m, n, k, fa, fw, seed):
+    """Activations whose 32-blocks have amax anywhere in 2**-127 .. 2**-110
+    (rows 0-15: every block; rows 16-31: every other block, the rest normal;
+    row 0's first block at exactly 2**-127, so E4M3 / E2M1 codes reach their
+    subnormal and smallest values), and weights with a few such rows."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_t(3, size=(m, k)) * 2.0
+    nb = k // 32
+    e = rng.integers(-127, -109, size=(32, nb)).astype(np.float64)
+    blk = a[:32].reshape(32, nb, 32)
+    amax = np.abs(blk).max(axis=2, keepdims=True)
+    tiny = blk / amax * 2.0 ** e[:, :, None]
+    tiny[16:, 1::2] = blk[16:, 1::2]                  # rows 16-31: every other block normal
+    tiny[0, 0] = blk[0, 0] / amax[0, 0] * 2.0 ** -127
+    a[:32] = tiny.reshape(32, k)
+    a = a.astype(np.float32)
+    w = rng.normal(0, 0.02, size=(n, k)).astype(np.float32)
+    w[5] *= 2.0 ** -110
+    w[7, :64] *= 2.0 ** -100
+    return oq.quantize(a, fa), oq.quantize(w, fw)
+
+
+@pytest.mark.parametrize("fa,fw", ROUTES)
+def test_gemm_tiny_block_scales(fa, fw):
+    """Blocks with amax down to 2**-127 (E8M0 codes near 0) on every route:
+    the MX dequantization must stay exact there (code 0 is 2**-127, and E4M3
+    values times a tiny scale must not underflow)."""
+    import fp8_quantized_linear_mxq_amd as mxq
+    m, n, k = 64, 96, 512
+    gu.say(f"gemm tiny scales {fa}x{fw} M={m} N={n} K={k}")
+    qa, qw = _tiny_operands(m, n, k, fa, fw, seed=29)
+    if fa != "NVFP4":
+        assert qa["scales"].min() == 0          # a code-0 block is present
+    y = mxq.gemm(gu.qtensor_from_oracle(qa, m, k), gu.qtensor_from_oracle(qw, n, k))
+    a_deq = gu.dequant_a_for_gemm(qa)
+    ref = np.abs(a_deq[:16] @ gu.dequant_w_for_gemm(qw).T)
+    if fa != "NVFP4":
+        # the tiny rows' outputs are far above the tolerance's absolute floor
+        assert np.median(ref) > 2.0 ** -126
+    r = gu.check_gemm(y, a_deq, gu.dequant_w_for_gemm(qw), gu.alpha_of(qa, qw),
+                      tag=f"{fa}x{fw} tiny")
+    gu.say(f"  worst err/tol {r:.3g}")

@@ -70,4 +70,16 @@ def test_grid_operands_exact_then_bf16():
 def test_tolerance_form():
     y = np.array([[2.0]])
     s = np.array([[10.0]])
-    assert og.tolerance(y, s)[0, 0] == 1e-5 * (1 + 2 ** -8) * 10.0 + 2 ** -8 * 2.0
+    assert og.tolerance(y, s)[0, 0] == 1e-5 * (1 + 2 ** -8) * 10.0 + 2 ** -8 * 2.0 + 2 ** -133
+
+
+def test_tolerance_covers_bf16_subnormal_rounding():
+    # rounding a tiny exact value to bfloat16 (subnormal below 2**-126, quantum
+    # 2**-133) errs by up to half a quantum; the tolerance's floor covers it
+    ys = np.array([[k * 2.0 ** -141 for k in range(1, 400, 7)] + [2.0 ** -134, 3 * 2.0 ** -134]])
+    err = np.abs(og.round_to_bf16(ys) - ys)
+    assert err.max() == 2.0 ** -134            # the ties: half a quantum
+    assert np.all(err <= og.tolerance(ys, np.zeros_like(ys)))
+    # a normal value's rounding stays within 2**-8 |y|
+    y = np.array([[1.0 + 2 ** -8]])
+    assert abs(og.round_to_bf16(y) - y)[0, 0] <= 2 ** -8 * y[0, 0]
