@@ -31,6 +31,7 @@ Module map:
   hadamard  Sylvester block-diagonal Hadamard rotation
   gemm      dequantized fp64 linear layer (+ low-rank branch) and its tolerance
   select    per-output-channel format choice by minimum reconstruction error
+  mse_scales  least-squared-error block (and NVFP4 tensor) scales for weights
   route     timestep-bucket activation-format lookup
 
 Parity unpinned (no independent pin possible): the GPU's MFMA-internal
@@ -38,4 +39,4 @@ summation order (bounded only by the stated tolerance) and near-tie format
 choices whose errors agree to 1e-12 relative.
 """
 
-from . import formats, quantize, hadamard, gemm, select, route  # noqa: F401
+from . import formats, quantize, hadamard, gemm, select, route, mse_scales  # noqa: F401
