@@ -22,8 +22,9 @@ block sizes or rounding rules; those readings are listed in each module):
   (16-bit low-rank branch next to the 4-bit residual GEMM).
 * "Bridging the Gap Between Promise and Performance for Microscaling FP4
   Quantization" summary (maximeter.ru), the two reasons FP4 fails (NVFP4's
-  small groups, MXFP4's power-of-two scales) and modification 3 (block-diagonal
-  Hadamard rotation of activations at inference).
+  small groups, MXFP4's power-of-two scales), modification 1 (least-MSE grid:
+  block and tensor scales optimised in turn) and modification 3
+  (block-diagonal Hadamard rotation of activations at inference).
 
 Module map:
   formats   E2M1 / E4M3 / E8M0 element and scale codes, round-to-nearest-even
