@@ -18,7 +18,7 @@ BF16 = 5   # unquantized bf16 activations (GEMM operand only)
 FORMATS = {"MXFP4": MXFP4, "MXFP8": MXFP8, "NVFP4": NVFP4, "INT4": INT4}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 DT_F32, DT_BF16 = 1, 2
-OP_QUANTIZE, OP_GEMM, OP_SELECT = 1, 2, 3
+OP_QUANTIZE, OP_GEMM, OP_SELECT, OP_QUANTIZE_MSE = 1, 2, 3, 4
 BLOCK = {MXFP4: 32, MXFP8: 32, NVFP4: 16, INT4: 32}
 
 STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARG", 2: "MXQ_ERR_UNSUPPORTED",
@@ -27,7 +27,7 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARG", 2: "MXQ_ERR_UNSUPPORTED",
 
 # Every symbol include/mxq.h declares.
 EXPORTS = ("mxq_quantize", "mxq_quantize_noalloc", "mxq_gemm", "mxq_gemm_mixed", "mxq_conv3x3_gemm_mixed",
-           "mxq_select_format",
+           "mxq_select_format", "mxq_quantize_mse",
            "mxq_act_format_for_step", "mxq_workspace_size", "mxq_storage",
            "mxq_status_string", "mxq_version")
 
@@ -78,6 +78,8 @@ def load():
     lib.mxq_select_format.argtypes = [vp, i32, i64, i64, i64, C.POINTER(i32), i32, vp, vp, vp,
                                       vp, vp, vp, sz, vp]
     lib.mxq_select_format.restype = i32
+    lib.mxq_quantize_mse.argtypes = [vp, i32, i64, i64, i64, qp, vp, sz, vp]
+    lib.mxq_quantize_mse.restype = i32
     lib.mxq_act_format_for_step.argtypes = [C.POINTER(C.c_uint8), i32, i32, i32, i32, i32]
     lib.mxq_act_format_for_step.restype = i32
     lib.mxq_workspace_size.argtypes = [i32, i64, i64, i32]
@@ -281,3 +283,23 @@ def select_format(w, candidates=(INT4, MXFP4, NVFP4), stream=None):
                                _ptr(ws), ws.numel(), _stream(stream))
     _check("mxq_select_format", st)
     return choice, sse, perm, counts, g
+
+
+def quantize_mse(w, fmt: int, out: QTensor | None = None, workspace=None,
+                 stream=None) -> QTensor:
+    """mxq_quantize_mse on 2-D torch weights (float32 or bfloat16, cuda):
+    MXFP4 or NVFP4 codes with least-squared-error scales."""
+    import torch
+    lib = load()
+    rows, cols = w.shape
+    dt = DT_BF16 if w.dtype == torch.bfloat16 else DT_F32
+    if out is None:
+        out = empty_qtensor(fmt, rows, cols, w.device)
+    if workspace is None:
+        n = workspace_size(OP_QUANTIZE_MSE, rows, cols, fmt)
+        workspace = torch.empty((max(n, 16),), dtype=torch.uint8, device=w.device)
+    qc = out.c()
+    st = lib.mxq_quantize_mse(_ptr(w), dt, rows, cols, w.stride(0), C.byref(qc),
+                              _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("mxq_quantize_mse", st)
+    return out

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxq.so")
-SOURCES = ["api.cpp", "quantize.hip", "lowrank.hip", "gemm_mx.hip", "gemm_dq.hip", "gemm_dqp.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "lowrank.hip", "gemm_mx.hip", "gemm_dq.hip", "gemm_dqp.hip",
+           "mse.hip"]
 ARCH = "gfx950"
 
 

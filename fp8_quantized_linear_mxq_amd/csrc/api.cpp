@@ -136,6 +136,9 @@ int64_t mxq_workspace_size(int32_t op, int64_t rows, int64_t cols, int32_t fmt) 
     case MXQ_OP_SELECT:
       // amax partials, the tensor scale, per-row SSE for up to 4 candidates
       return (int64_t)kAmaxPartials * 4 + 64 + rows * 4 * 8;
+    case MXQ_OP_QUANTIZE_MSE:
+      if (fmt != MXQ_FMT_MXFP4 && fmt != MXQ_FMT_NVFP4) return -1;
+      return mse_workspace_bytes(fmt, rows);
     default:
       return -1;
   }
@@ -415,6 +418,45 @@ mxq_status mxq_conv3x3_gemm_mixed(const mxq_qtensor* x, int64_t height, int64_t 
     off += w->rows;
   }
   return MXQ_OK;
+}
+
+mxq_status mxq_quantize_mse(const void* w, int32_t dtype, int64_t rows, int64_t cols,
+                            int64_t ldw, mxq_qtensor* out, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  if (!out || (dtype != MXQ_DT_F32 && dtype != MXQ_DT_BF16) || rows < 0 || cols < 0)
+    return MXQ_ERR_INVALID_ARG;
+  if (out->fmt != MXQ_FMT_MXFP4 && out->fmt != MXQ_FMT_NVFP4)
+    return known_fmt(out->fmt) ? MXQ_ERR_UNSUPPORTED : MXQ_ERR_INVALID_ARG;
+  if (out->rows != rows || out->cols != cols) return MXQ_ERR_INVALID_ARG;
+  if (cols % 32) return MXQ_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MXQ_OK;
+  if (rows * (cols / 8) >= (int64_t)1 << 32) return MXQ_ERR_SHAPE;
+  if (!w || ldw < cols) return MXQ_ERR_INVALID_ARG;
+  const int esz = dtype == MXQ_DT_F32 ? 4 : 2;
+  if (!aligned(w, 16) || (ldw * esz) % 16) return MXQ_ERR_ALIGNMENT;
+  mxq_status st = check_qtensor(out);
+  if (st != MXQ_OK) return st;
+  const int64_t need = mse_workspace_bytes(out->fmt, rows);
+  if (need > 0 && (!workspace || ws_bytes < (size_t)need || !aligned(workspace, 16)))
+    return MXQ_ERR_WORKSPACE;
+  unsigned* dbg = nullptr;
+  st = device_entry(&dbg);
+  if (st != MXQ_OK) return st;
+  MseArgs a;
+  a.x = w;
+  a.dtype = dtype;
+  a.rows = rows;
+  a.cols = cols;
+  a.ldx = ldw;
+  a.fmt = out->fmt;
+  a.codes = static_cast<uint8_t*>(out->codes);
+  a.ld_codes = out->ld_codes;
+  a.scales = static_cast<uint8_t*>(out->scales);
+  a.ld_scales = out->ld_scales;
+  a.tensor_scale_out = out->tensor_scale;
+  a.ws = workspace;
+  a.dbg = dbg;
+  return from_hip(launch_quantize_mse(a, as_stream(stream)));
 }
 
 mxq_status mxq_select_format(const void* w, int32_t dtype, int64_t n, int64_t k, int64_t ldw,

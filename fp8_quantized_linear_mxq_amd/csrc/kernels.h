@@ -87,4 +87,27 @@ struct SelectArgs {
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
+// NVFP4 dynamic tensor scale g = RN_fp32(max |x| / 2688) of a [rows, cols]
+// tensor (cols a multiple of 32) written to g_out; partials: kAmaxPartials
+// floats of workspace.
+hipError_t launch_nvfp4_tensor_scale(const void* x, int dtype, int64_t rows, int64_t cols,
+                                     int64_t ldx, float* partials, float* g_out,
+                                     unsigned* dbg, hipStream_t s);
+
+// Weights with least-squared-error scales (MXFP4: block step; NVFP4: block,
+// tensor, block).  Workspace (NVFP4): kAmaxPartials floats, then 2 * rows
+// doubles (per-row sums of the tensor step), 16-byte aligned.
+struct MseArgs {
+  const void* x; int dtype;
+  int64_t rows, cols, ldx;
+  int fmt;
+  uint8_t* codes; int64_t ld_codes;
+  uint8_t* scales; int64_t ld_scales;
+  float* tensor_scale_out;   // NVFP4
+  void* ws;
+  unsigned* dbg;
+};
+int64_t mse_workspace_bytes(int fmt, int64_t rows);
+hipError_t launch_quantize_mse(const MseArgs& a, hipStream_t s);
+
 }  // namespace mxq

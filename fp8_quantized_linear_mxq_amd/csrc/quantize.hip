@@ -689,6 +689,13 @@ __global__ __launch_bounds__(256) void group_kernel(const uint8_t* choice, int n
   }
 }
 
+// g = RN_fp32(A / 2688) from the phase-1 partial maxima, written to g_out
+// (one workgroup).
+__global__ __launch_bounds__(kThreads) void tensor_scale_kernel(QParams p) {
+  const float g = (float)((double)reduce_partials(p) / 2688.0);
+  if (threadIdx.x == 0) *p.g_out = g;
+}
+
 template <int DT, int FMT>
 hipError_t dispatch_had(int had, dim3 grid, const QParams& p, uint32_t bpr, uint32_t nblk,
                         hipStream_t s) {
@@ -830,6 +837,32 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
              : dispatch_fmt<DT_F32>(a.fmt, a.hadamard_n, dim3(blocks), p, bpr, nblk, s);
 }
 
+
+hipError_t launch_nvfp4_tensor_scale(const void* x, int dtype, int64_t rows, int64_t cols,
+                                     int64_t ldx, float* partials, float* g_out,
+                                     unsigned* dbg, hipStream_t s) {
+  QParams p;
+  p.x = x;
+  p.ldx = ldx;
+  p.cpr = (uint32_t)(cols / 8);
+  p.total = (uint32_t)(rows * (cols / 8));
+  p.codes = nullptr; p.ld_codes = 0; p.scales = nullptr; p.ld_scales = 0;
+  p.g_out = g_out;
+  p.g_static = nullptr;
+  p.partials = partials;
+  p.dbg = dbg;
+  const uint32_t bpr = (uint32_t)(cols / 32), nblk = (uint32_t)(rows * bpr);
+  uint32_t blocks = (nblk + kThreads - 1) / kThreads;
+  if (blocks > (uint32_t)kAmaxPartials) blocks = kAmaxPartials;
+  if (blocks == 0) return hipSuccess;
+  p.n_partials = (int)blocks;
+  hipError_t e = (dtype == DT_BF16)
+                     ? dispatch_amax<DT_BF16>(0, dim3(blocks), p, partials, bpr, nblk, s)
+                     : dispatch_amax<DT_F32>(0, dim3(blocks), p, partials, bpr, nblk, s);
+  if (e != hipSuccess) return e;
+  tensor_scale_kernel<<<1, kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   SelParams sp;

@@ -280,6 +280,36 @@ mxq_status mxq_conv3x3_gemm_mixed(const mxq_qtensor* x, int64_t height, int64_t 
                                   size_t ws_bytes, void* stream);
 
 /*
+ * mxq_quantize_mse -- quantize weights [rows, cols] to MXFP4 or NVFP4 with
+ * least-squared-error scales instead of the amax rule ("Bridging the Gap
+ * ... Microscaling FP4 Quantization" summary, MR-GPTQ modification 1: the
+ * grid is chosen for least MSE by optimising block and tensor scales in
+ * turn).  Weight preparation, once per layer.
+ *
+ * Block step: each block's scale code is, among every code of its format
+ * (E8M0 0..254; E4M3 0..126 times g), the one whose squared error
+ * sum_i (x_i - x_hat_i)^2 -- taken over the block in element order, each
+ * subtraction, product and addition rounded to float64 separately -- is
+ * smallest, ties to the smaller code; elements then round to nearest even
+ * under that scale.  NVFP4 adds a tensor step: with the codes fixed,
+ * g = RN_fp32(P / Q), P = sum x w, Q = sum w^2 (w = element value times its
+ * block scale), float64 sums of row sums taken in order (Q = 0, or a
+ * quotient that rounds to zero, keeps g).  Rounds: NVFP4 amax-rule g, block
+ * step, tensor step, block step (g written to *out->tensor_scale); MXFP4
+ * one block step.  Never a larger total squared error than the amax rule.
+ *
+ *  w, dtype, ldw   as mxq_quantize's x (fp32 or bf16, 16-byte aligned).
+ *  out         out->fmt MXQ_FMT_MXFP4 or MXQ_FMT_NVFP4 (others:
+ *              MXQ_ERR_UNSUPPORTED); buffers as for mxq_quantize.
+ *  workspace   mxq_workspace_size(MXQ_OP_QUANTIZE_MSE, rows, cols, fmt)
+ *              bytes, 16-byte aligned (none for MXFP4).
+ * cols must be a multiple of 32.
+ */
+mxq_status mxq_quantize_mse(const void* w, int32_t dtype, int64_t rows, int64_t cols,
+                            int64_t ldw, mxq_qtensor* out, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/*
  * mxq_select_format -- per-output-channel weight format by least
  * reconstruction error (Chameleon article, "the format is chosen by the
  * value distribution").
@@ -315,7 +345,7 @@ int32_t mxq_act_format_for_step(const uint8_t* table, int32_t n_layers, int32_t 
                                 int32_t layer, int32_t step, int32_t num_steps);
 
 /* Operations for mxq_workspace_size. */
-enum { MXQ_OP_QUANTIZE = 1, MXQ_OP_GEMM = 2, MXQ_OP_SELECT = 3 };
+enum { MXQ_OP_QUANTIZE = 1, MXQ_OP_GEMM = 2, MXQ_OP_SELECT = 3, MXQ_OP_QUANTIZE_MSE = 4 };
 
 /* Workspace bytes an operation needs for a [rows, cols] operand of format
  * fmt (0 when none); for MXQ_OP_GEMM rows = M, cols = N (weight rows) and
