@@ -33,6 +33,7 @@ Module map:
   gemm      dequantized fp64 linear layer (+ low-rank branch) and its tolerance
   select    per-output-channel format choice by minimum reconstruction error
   mse_scales  least-squared-error block (and NVFP4 tensor) scales for weights
+  lowrank   offline SVDQuant split W ~= (L1 L2)^T + R (truncated SVD)
   route     timestep-bucket activation-format lookup
 
 Parity unpinned (no independent pin possible): the GPU's MFMA-internal
@@ -40,4 +41,4 @@ summation order (bounded only by the stated tolerance) and near-tie format
 choices whose errors agree to 1e-12 relative.
 """
 
-from . import formats, quantize, hadamard, gemm, select, route, mse_scales  # noqa: F401
+from . import formats, quantize, hadamard, gemm, select, route, mse_scales, lowrank  # noqa: F401
