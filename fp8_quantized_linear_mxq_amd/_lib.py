@@ -18,7 +18,7 @@ BF16 = 5   # unquantized bf16 activations (GEMM operand only)
 FORMATS = {"MXFP4": MXFP4, "MXFP8": MXFP8, "NVFP4": NVFP4, "INT4": INT4}
 FORMAT_NAMES = {v: k for k, v in FORMATS.items()}
 DT_F32, DT_BF16 = 1, 2
-OP_QUANTIZE, OP_GEMM, OP_SELECT, OP_QUANTIZE_MSE = 1, 2, 3, 4
+OP_QUANTIZE, OP_GEMM, OP_SELECT, OP_QUANTIZE_MSE, OP_LOWRANK_SPLIT = 1, 2, 3, 4, 5
 BLOCK = {MXFP4: 32, MXFP8: 32, NVFP4: 16, INT4: 32}
 
 STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARG", 2: "MXQ_ERR_UNSUPPORTED",
@@ -27,7 +27,7 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARG", 2: "MXQ_ERR_UNSUPPORTED",
 
 # Every symbol include/mxq.h declares.
 EXPORTS = ("mxq_quantize", "mxq_quantize_noalloc", "mxq_gemm", "mxq_gemm_mixed", "mxq_conv3x3_gemm_mixed",
-           "mxq_select_format", "mxq_quantize_mse",
+           "mxq_select_format", "mxq_quantize_mse", "mxq_lowrank_split",
            "mxq_act_format_for_step", "mxq_workspace_size", "mxq_storage",
            "mxq_status_string", "mxq_version")
 
@@ -80,6 +80,8 @@ def load():
     lib.mxq_select_format.restype = i32
     lib.mxq_quantize_mse.argtypes = [vp, i32, i64, i64, i64, qp, vp, sz, vp]
     lib.mxq_quantize_mse.restype = i32
+    lib.mxq_lowrank_split.argtypes = [vp, i64, i64, i64, i32, i32, vp, vp, vp, i64, vp, vp, sz, vp]
+    lib.mxq_lowrank_split.restype = i32
     lib.mxq_act_format_for_step.argtypes = [C.POINTER(C.c_uint8), i32, i32, i32, i32, i32]
     lib.mxq_act_format_for_step.restype = i32
     lib.mxq_workspace_size.argtypes = [i32, i64, i64, i32]
@@ -303,3 +305,24 @@ def quantize_mse(w, fmt: int, out: QTensor | None = None, workspace=None,
                               _ptr(workspace), workspace.numel(), _stream(stream))
     _check("mxq_quantize_mse", st)
     return out
+
+
+def lowrank_split(w, rank: int, iters: int = 0, stream=None):
+    """mxq_lowrank_split on 2-D float32 cuda weights [n, k]; returns
+    (L1^T bf16 [rank, k], L2^T bf16 [n, rank], R float32 [n, k],
+    sigma float32 [rank])."""
+    import torch
+    lib = load()
+    n, k = w.shape
+    dev = w.device
+    l1t = torch.empty((rank, k), dtype=torch.bfloat16, device=dev)
+    l2t = torch.empty((n, rank), dtype=torch.bfloat16, device=dev)
+    resid = torch.empty((n, k), dtype=torch.float32, device=dev)
+    sigma = torch.empty((rank,), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(workspace_size(OP_LOWRANK_SPLIT, n, k, rank), 256),),
+                     dtype=torch.uint8, device=dev)
+    st = lib.mxq_lowrank_split(_ptr(w), n, k, w.stride(0), rank, iters, _ptr(l1t), _ptr(l2t),
+                               _ptr(resid), resid.stride(0), _ptr(sigma), _ptr(ws), ws.numel(),
+                               _stream(stream))
+    _check("mxq_lowrank_split", st)
+    return l1t, l2t, resid, sigma

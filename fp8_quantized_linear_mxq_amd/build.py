@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxq.so")
 SOURCES = ["api.cpp", "quantize.hip", "lowrank.hip", "gemm_mx.hip", "gemm_dq.hip", "gemm_dqp.hip",
-           "mse.hip"]
+           "mse.hip", "lowrank_split.hip"]
 ARCH = "gfx950"
 
 

@@ -136,6 +136,10 @@ int64_t mxq_workspace_size(int32_t op, int64_t rows, int64_t cols, int32_t fmt) 
     case MXQ_OP_SELECT:
       // amax partials, the tensor scale, per-row SSE for up to 4 candidates
       return (int64_t)kAmaxPartials * 4 + 64 + rows * 4 * 8;
+    case MXQ_OP_LOWRANK_SPLIT:
+      // rows = N, cols = K, fmt = the rank
+      if (fmt < 1 || fmt > 128 || fmt > rows || fmt > cols) return -1;
+      return lowrank_split_workspace(rows, cols, fmt);
     case MXQ_OP_QUANTIZE_MSE:
       if (fmt != MXQ_FMT_MXFP4 && fmt != MXQ_FMT_NVFP4) return -1;
       return mse_workspace_bytes(fmt, rows);
@@ -457,6 +461,37 @@ mxq_status mxq_quantize_mse(const void* w, int32_t dtype, int64_t rows, int64_t 
   a.ws = workspace;
   a.dbg = dbg;
   return from_hip(launch_quantize_mse(a, as_stream(stream)));
+}
+
+mxq_status mxq_lowrank_split(const float* w, int64_t n, int64_t k, int64_t ldw, int32_t rank,
+                             int32_t iters, void* l1t, void* l2t, float* resid, int64_t ld_resid,
+                             float* sigma, void* workspace, size_t ws_bytes, void* stream) {
+  if (n < 0 || k < 0 || rank < 1 || rank > 128 || iters < 0 || iters > 64)
+    return MXQ_ERR_INVALID_ARG;
+  if (rank > n || rank > k) return MXQ_ERR_SHAPE;
+  if (!w || !l1t || !l2t || !resid || ldw < k || ld_resid < k) return MXQ_ERR_INVALID_ARG;
+  if (!aligned(w, 4) || !aligned(l1t, 2) || !aligned(l2t, 2) || !aligned(resid, 4) ||
+      (sigma && !aligned(sigma, 4)))
+    return MXQ_ERR_ALIGNMENT;
+  const int64_t need = lowrank_split_workspace(n, k, rank);
+  if (!workspace || ws_bytes < (size_t)need || !aligned(workspace, 256)) return MXQ_ERR_WORKSPACE;
+  unsigned* dbg = nullptr;
+  const mxq_status st = device_entry(&dbg);
+  if (st != MXQ_OK) return st;
+  LowrankSplitArgs a;
+  a.w = w;
+  a.n = n;
+  a.k = k;
+  a.ldw = ldw;
+  a.rank = rank;
+  a.iters = iters == 0 ? 8 : iters;
+  a.l1t = static_cast<uint16_t*>(l1t);
+  a.l2t = static_cast<uint16_t*>(l2t);
+  a.resid = resid;
+  a.ld_resid = ld_resid;
+  a.sigma = sigma;
+  a.ws = workspace;
+  return from_hip(launch_lowrank_split(a, as_stream(stream)));
 }
 
 mxq_status mxq_select_format(const void* w, int32_t dtype, int64_t n, int64_t k, int64_t ldw,

@@ -108,6 +108,20 @@ struct MseArgs {
   unsigned* dbg;
 };
 int64_t mse_workspace_bytes(int fmt, int64_t rows);
+
+// Offline SVD split W [n][k] ~= (L1 L2)^T + R (rank-r truncated SVD by
+// subspace iteration).
+struct LowrankSplitArgs {
+  const float* w; int64_t n, k, ldw;
+  int rank, iters;
+  uint16_t* l1t;      // bf16 [rank][k]
+  uint16_t* l2t;      // bf16 [n][rank]
+  float* resid; int64_t ld_resid;
+  float* sigma;       // optional [rank]
+  void* ws;
+};
+int64_t lowrank_split_workspace(int64_t n, int64_t k, int rank);
+hipError_t launch_lowrank_split(const LowrankSplitArgs& a, hipStream_t s);
 hipError_t launch_quantize_mse(const MseArgs& a, hipStream_t s);
 
 }  // namespace mxq

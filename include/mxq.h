@@ -310,6 +310,33 @@ mxq_status mxq_quantize_mse(const void* w, int32_t dtype, int64_t rows, int64_t 
                             void* stream);
 
 /*
+ * mxq_lowrank_split -- offline SVDQuant split of a weight (Nunchaku article,
+ * "main explanation": the hardest part of the weight is kept as a low-rank
+ * 16-bit branch and the rest is quantized to 4 bits):
+ *   W [n][k] ~= (L1 L2)^T + R,  L1 = V_r sqrt(S_r) [k][r],  L2 = sqrt(S_r) U_r^T [r][n],
+ * from the rank-r truncated SVD W_r = U_r S_r V_r^T, factors rounded to
+ * bf16, R = W - (L1 L2)^T in fp32 (then quantize R with mxq_quantize or
+ * mxq_quantize_mse).  The subspace comes from `iters` rounds of subspace
+ * iteration from a fixed start (r + 16 columns) and a Rayleigh-Ritz step
+ * (float64 Jacobi); it converges to the truncated SVD when sigma_r is well
+ * above sigma_{r+17}.  Singular pairs carry an arbitrary sign; L1 L2 and R do
+ * not depend on it.  Weight preparation, once per layer.
+ *
+ *  w           device fp32 [n][ldw] (k columns used), 4-byte aligned.
+ *  rank        1..128, at most min(n, k).   iters  0 (default 8) .. 64.
+ *  l1t         device bf16 [rank][k]: L1^T, the layout mxq_quantize's
+ *              lr_l1t takes.
+ *  l2t         device bf16 [n][rank]: L2^T, the layout mxq_gemm's lr_l2t takes.
+ *  resid       device fp32 [n][ld_resid]: R.
+ *  sigma       optional device fp32 [rank]: the singular values, decreasing.
+ *  workspace   mxq_workspace_size(MXQ_OP_LOWRANK_SPLIT, n, k, rank) bytes,
+ *              256-byte aligned.
+ */
+mxq_status mxq_lowrank_split(const float* w, int64_t n, int64_t k, int64_t ldw, int32_t rank,
+                             int32_t iters, void* l1t, void* l2t, float* resid, int64_t ld_resid,
+                             float* sigma, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * mxq_select_format -- per-output-channel weight format by least
  * reconstruction error (Chameleon article, "the format is chosen by the
  * value distribution").
@@ -345,11 +372,13 @@ int32_t mxq_act_format_for_step(const uint8_t* table, int32_t n_layers, int32_t 
                                 int32_t layer, int32_t step, int32_t num_steps);
 
 /* Operations for mxq_workspace_size. */
-enum { MXQ_OP_QUANTIZE = 1, MXQ_OP_GEMM = 2, MXQ_OP_SELECT = 3, MXQ_OP_QUANTIZE_MSE = 4 };
+enum { MXQ_OP_QUANTIZE = 1, MXQ_OP_GEMM = 2, MXQ_OP_SELECT = 3, MXQ_OP_QUANTIZE_MSE = 4,
+       MXQ_OP_LOWRANK_SPLIT = 5 };
 
 /* Workspace bytes an operation needs for a [rows, cols] operand of format
  * fmt (0 when none); for MXQ_OP_GEMM rows = M, cols = N (weight rows) and
- * fmt = the weight format (the optional split-K workspace).  Returns -1 for
+ * fmt = the weight format (the optional split-K workspace); for
+ * MXQ_OP_LOWRANK_SPLIT rows = n, cols = k and fmt = the rank.  Returns -1 for
  * unknown arguments.  Host-only. */
 int64_t mxq_workspace_size(int32_t op, int64_t rows, int64_t cols, int32_t fmt);
 
