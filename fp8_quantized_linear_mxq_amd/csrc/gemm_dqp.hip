@@ -229,6 +229,7 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
     }
   }
 
+  const uint8_t* zsrc = zero_src();
   auto issue = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
     const bool past = kt >= KT;   // past the end of K: a tile of zeros
     kt = past ? KT - 1 : kt;
@@ -242,11 +243,11 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
         const int idx = t * NW + wave;
         const bool real = (TOTAL % NW == 0) || idx < TOTAL;
         const bool in = !past && conv_inside(cv_m[t], tp);
-        const uint8_t* src = in ? cv_code[t] + off : g_zero16;
+        const uint8_t* src = in ? cv_code[t] + off : zsrc;
         uint8_t* dst = real ? st + idx * 64 * 16 : pad;
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
       }
-      issue_tile<TBN, W_RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad);
+      issue_tile<TBN, W_RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, zsrc, past, pad);
       // scales: activation rows through the tap, weight rows as issue_scale_tile
       const int64_t soff = (int64_t)tp.shift * p.ldas + tp.kc * SBA;
       uint8_t* region = st + A_STAGE + W_STAGE;
@@ -256,23 +257,23 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
         const int d = slot0 + lane;
         const uint8_t* src;
         if (d < S_DA) {
-          src = conv_inside(cv_sm[t], tp) ? cv_scl[t] + soff : g_zero16;
+          src = conv_inside(cv_sm[t], tp) ? cv_scl[t] + soff : zsrc;
         } else if (d < S_D) {
           const int e = d - S_DA;
           int r = n0 + e / (SBW / 4);
           r = r < p.N ? r : p.N - 1;
           src = p.ws + (int64_t)r * p.ldws + kt * SBW + (e % (SBW / 4)) * 4;
         } else {
-          src = g_zero16;
+          src = zsrc;
         }
-        src = past ? g_zero16 : src;
+        src = past ? zsrc : src;
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + slot0 * 4), 4, 0, 0);
       }
     } else {
-      issue_tile<TBM, A_RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad);
-      issue_tile<TBN, W_RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad);
+      issue_tile<TBM, A_RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, zsrc, past, pad);
+      issue_tile<TBN, W_RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, zsrc, past, pad);
       issue_scale_tile<TBM, SBA, TBN, SBW, NW>(p, m0, n0, kt, st + A_STAGE + W_STAGE, wave, lane,
-                                               past);
+                                               zsrc, past);
     }
   };
 

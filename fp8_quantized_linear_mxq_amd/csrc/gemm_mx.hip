@@ -52,6 +52,59 @@ constexpr int KS = BK / 64;       // MFMA K-steps per K-tile
 constexpr int SB = BK / 32;       // scale bytes per row per K-tile
 constexpr int kSlab = 8;          // K-tiles per fp32 slab when slabbing
 
+// Whole-tile staged epilogue (no column map; 16-byte aligned output rows):
+// each wave writes its accumulators (+ bias, bf16) into the LDS image of the
+// workgroup tile -- rows [0, TBM/2) in `lo`, the rest in `hi` -- then every
+// thread stores 16-byte pieces of whole tile rows with non-temporal stores.
+// Accumulator layout (D^T = W A^T): lane l of MFMA tile (i, j) holds row
+// i*32 + l%32 and columns j*32 + 8g + 4(l/32) + [0, 4) at acc[i][j][4g..4g+3].
+template <int TM, int TN, int WGM, int STAGE>
+__device__ __forceinline__ void epilogue_wg(const GemmP& p, v16f (&acc)[TM][TN], int m0, int n0,
+                                            int wm, int wn, int lane, uint8_t* lo, uint8_t* hi) {
+  constexpr int TBM = 32 * TM * WGM, TBN = 64 * TN, NT = 128 * WGM;
+  constexpr int WRS = TBN * 2 + 16, CPR = TBN / 8;   // row stride; 16-byte pieces per row
+  const int l32 = lane & 31, half = lane >> 5;
+  const int n_lim = p.N < p.n_out ? p.N : p.n_out;
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int r = wm * 32 * TM + i * 32 + l32;
+    uint8_t* row = (r < TBM / 2 ? lo + r * WRS : hi + (r - TBM / 2) * WRS);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = wn * 32 * TN + j * 32 + 8 * g + 4 * half;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int nn = n0 + c + e;
+          v[e] = acc[i][j][4 * g + e] + ((p.bias && nn < n_lim) ? bf16_bits_to_f32(p.bias[nn]) : 0.f);
+        }
+        uint2 pk;
+        pk.x = pack_bf16_rne(v[0], v[1]);
+        pk.y = pack_bf16_rne(v[2], v[3]);
+        *reinterpret_cast<uint2*>(row + c * 2) = pk;
+      }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < TBM * CPR; idx += NT) {
+    const int r = idx / CPR, ch = idx % CPR;
+    const uint8_t* src = (r < TBM / 2 ? lo + r * WRS : hi + (r - TBM / 2) * WRS) + ch * 16;
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    const int row = m0 + r, n = n0 + ch * 8;
+    if (row >= p.M) continue;
+    uint16_t* o = p.out + (int64_t)row * p.ld_out + n;
+    if (n + 8 <= n_lim) {
+      __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(o));
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < n_lim) o[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
 template <int TM, int TN, int WGM, bool SLAB, bool LR, bool VSC>
 __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) {
   constexpr int NW = 2 * WGM;                      // waves: WGM (rows) x 2 (columns)
@@ -87,6 +140,7 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   // lane reads is l32 plus a multiple of 32, all with the same swizzle, so
   // one register per K-step serves all of them (the rows differ by constant
   // offsets).
+  const uint8_t* zsrc = zero_src();
   const int swl = swz<CH>(l32);
   uint32_t a_base[KS], w_base[KS];
 #pragma unroll
@@ -103,8 +157,8 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
     kt = past ? KT - 1 : kt;
     const int lim = kt == KT - 1 ? last_ch : CH;
     uint8_t* pad = st + A_STAGE + W_STAGE;
-    issue_tile<TBM, RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, past, pad, lim);
-    issue_tile<TBN, RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, past, pad, lim);
+    issue_tile<TBM, RB, NW>(p.a, p.lda, m0, p.M, kt, st, wave, lane, zsrc, past, pad, lim);
+    issue_tile<TBN, RB, NW>(p.w, p.ldw, n0, p.N, kt, st + A_STAGE, wave, lane, zsrc, past, pad, lim);
   };
   // Scale group g (K-tiles gG .. gG+G-1) into buffer g % 2: rows of A, then
   // rows of W, SROW bytes each.  VSC (16-byte aligned scale rows, K a
@@ -129,7 +183,7 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
       const uint8_t* pa = p.as + (int64_t)ra * p.ldas;
       const uint8_t* pw = p.ws + (int64_t)rw * p.ldws;
       const uint8_t* src = (r < TBM ? pa : pw) + k0 + q * PB;
-      src = real && k0 + q * PB < srow_bytes ? src : g_zero16;
+      src = real && k0 + q * PB < srow_bytes ? src : zsrc;
       uint8_t* dst = real ? buf + idx * 64 * PB : scl + 2 * SGRP;
       if constexpr (VSC) __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
       else __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 4, 0, 0);
@@ -212,13 +266,17 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   constexpr int N_MFMA = KS * TM * TN;
   constexpr int N_DS0 = TM + TN;                  // K-step 0
   constexpr int N_DS1 = (KS - 1) * (TM + TN);     // K-steps 1 .. KS-1
-  auto step = [&](int kt, const uint8_t* st_cur, uint8_t* st_nxt, bool even) __attribute__((always_inline)) {
+  // K-tile 1 is issued in the prologue, so the first step waits only for
+  // K-tile 0 and issues no codes
+  auto step = [&](int kt, const uint8_t* st_cur, uint8_t* st_nxt, bool even, bool first) __attribute__((always_inline)) {
     // nothing of the previous step sinks below the wait
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<0>();
+    if (first) wait_vmcnt<NT>();
+    else wait_vmcnt<0>();
     read_scales(kt);
     __builtin_amdgcn_s_barrier();
-    issue(kt + 1, st_nxt);
+    asm volatile("" ::: "memory");   // no LDS read moves above the barrier
+    if (!first) issue(kt + 1, st_nxt);
     if (even) issue_scales(kt / G + 1);
     compute(st_cur);
     // K-step 0 first; then one MFMA, one fragment read (running a K-step
@@ -243,17 +301,34 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
     }
   };
 
-  // The low-rank branch goes into the accumulators first, its operands (up
-  // to 32 ranks at once) loaded right behind the first K-tile, so both
-  // latencies overlap and the MFMAs run while the pipeline fills.
+  // Prologue: K-tile 0, scale group 0, the low-rank operands (up to 32
+  // ranks), then K-tile 1 into the other stage.  The low-rank branch goes
+  // into the accumulators first, its MFMAs running while K-tile 1 is in
+  // flight (the loads complete in issue order, so waiting for all but
+  // K-tile 1's NT loads covers everything before them).
   issue(0, st0);
   issue_scales(0);
-  if constexpr (LR) add_lowrank<TM, TN>(p, acc, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane);
-  wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();   // scale group 0 visible to every wave
-  for (int kt = 0; kt < KT; kt += 2) {
-    step(kt, st0, st1, true);
-    step(kt + 1, st1, st0, false);
+  LrFrag<TM, TN> lrf;
+  const int lr_nt = LR ? (p.rank / 16 < 2 ? p.rank / 16 : 2) : 0;
+  if constexpr (LR) lr_load<TM, TN>(p, lrf, 0, lr_nt, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane);
+  issue(1, st1);
+  wait_vmcnt<NT>();
+  if constexpr (LR) {
+    lr_mma<TM, TN>(lrf, lr_nt, acc);
+    // ranks past the first 32 (rare): their own loads and waits
+    for (int t0 = 2; t0 < p.rank / 16; t0 += 2) {
+      LrFrag<TM, TN> f;
+      const int nt = p.rank / 16 - t0 < 2 ? p.rank / 16 - t0 : 2;
+      lr_load<TM, TN>(p, f, t0, nt, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane);
+      lr_mma<TM, TN>(f, nt, acc);
+    }
+  }
+  __builtin_amdgcn_s_barrier();   // K-tile 0 and scale group 0 visible to every wave
+  step(0, st0, st1, true, true);
+  step(1, st1, st0, false, false);
+  for (int kt = 2; kt < KT; kt += 2) {
+    step(kt, st0, st1, true, false);
+    step(kt + 1, st1, st0, false, false);
   }
   wait_vmcnt<0>();   // the zero loads issued past the end
   if constexpr (SLAB) {
@@ -266,6 +341,18 @@ __global__ __launch_bounds__(128 * WGM, 1) void gemm_mx_kernel(GemmP p, int gm) 
   // each wave stages its output rows in its own slice of one of them
   wait_lgkmcnt0();
   __syncthreads();
+  // The workgroup's whole output tile goes through LDS (its upper half of
+  // rows in one stage, the lower half in the other) and leaves as 16-byte
+  // pieces of whole rows, so every 128-byte line of the output is written
+  // by one store instruction (a per-wave staging splits the lines that
+  // straddle two waves' columns).
+  constexpr int WRS = TBN * 2 + 16;            // LDS bytes per staged row (padded)
+  if constexpr ((TBM / 2) * WRS <= STAGE) {
+    if (!p.col_map && (p.ld_out & 7) == 0 && (reinterpret_cast<uintptr_t>(p.out) & 15) == 0) {
+      epilogue_wg<TM, TN, WGM, STAGE>(p, acc, m0, n0, wm, wn, lane, st0, st1);
+      return;
+    }
+  }
   constexpr int RG = 32 * (TN * 64 + 16), SL = STAGE / RG;   // staging slices per stage
   static_assert(2 * SL >= NW, "a staging slice per wave");
   uint8_t* region = (wave / SL == 0 ? st0 : st1) + (wave % SL) * RG;

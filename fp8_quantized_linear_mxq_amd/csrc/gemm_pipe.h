@@ -26,6 +26,20 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC
 // main loop needs no branch.
 static __device__ uint8_t g_zero16[16];
 
+// The address of g_zero16 held in two VGPRs for the life of a kernel.  The
+// symbol is reached through the GOT, and left to itself the compiler reloads
+// it with a scalar load inside the main loop; a scalar load in flight turns
+// every LDS wait in the loop into a full drain (LDS reads and scalar loads
+// share one counter, and scalar loads may return out of order), so each
+// MFMA group would wait for the fragment reads just issued for the next step.
+__device__ __forceinline__ const uint8_t* zero_src() {
+  const uint64_t a = reinterpret_cast<uint64_t>(g_zero16);
+  uint32_t lo = (uint32_t)a, hi = (uint32_t)(a >> 32);
+  asm volatile("" : "+v"(lo));
+  asm volatile("" : "+v"(hi));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
+}
+
 // Direct loads of one operand tile (ROWS rows x RB bytes of K-tile kt) into
 // an LDS stage.  The tile is ROWS*CH/64 64-lane instructions, dealt to the NW
 // waves round-robin; slot L (16 bytes) of the stage holds row L / CH, physical
@@ -42,8 +56,8 @@ constexpr int tile_loads() { return (ROWS * RB / 1024 + NW - 1) / NW; }
 template <int ROWS, int RB, int NW = 4>
 __device__ __forceinline__ void issue_tile(const uint8_t* base, int64_t ld, int row0, int nrows,
                                            int kt, uint8_t* stage, int wave, int lane,
-                                           bool zero = false, uint8_t* pad = nullptr,
-                                           int lim = RB / 16) {
+                                           const uint8_t* zsrc, bool zero = false,
+                                           uint8_t* pad = nullptr, int lim = RB / 16) {
   constexpr int CH = RB / 16;
   constexpr int TOTAL = ROWS * CH / 64;
   static_assert(ROWS * CH % 64 == 0, "tile must split into whole 64-lane loads");
@@ -59,7 +73,7 @@ __device__ __forceinline__ void issue_tile(const uint8_t* base, int64_t ld, int 
     const int lc = pc ^ swz<CH>(r);
     const uint8_t* src = base + (int64_t)grow * ld + (int64_t)kt * RB + lc * 16;
     const bool cut = lim < RB / 16 && lc >= lim;
-    src = (zero || !real || cut) ? g_zero16 : src;
+    src = (zero || !real || cut) ? zsrc : src;
     uint8_t* dst = real ? stage + slot0 * 16 : pad;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)dst, 16, 0, 0);
   }
@@ -69,11 +83,13 @@ __device__ __forceinline__ void issue_tile(const uint8_t* base, int64_t ld, int 
 // per lane: TBM rows of A (SBA bytes each), then TBN rows of W (SBW bytes
 // each); lanes past the end re-read a valid dword into padding; with `zero`
 // set every lane reads zeros, and so do dwords at or past dword `lim_a` of
-// an A row or `lim_w` of a W row (a K-tile cut short by the end of K).  Issues
+// an A row or `lim_w` of a W row (a K-tile cut short by the end of K); zeros
+// come from zsrc (zero_src()).  Issues
 // ceil((TBM*SBA + TBN*SBW) / (256*NW)) loads per wave.
 template <int TBM, int SBA, int TBN, int SBW, int NW = 4>
 __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0, int kt,
                                                  uint8_t* region, int wave, int lane,
+                                                 const uint8_t* zsrc,
                                                  bool zero = false, int lim_a = SBA / 4,
                                                  int lim_w = SBW / 4) {
   constexpr int DA = TBM * SBA / 4, D = DA + TBN * SBW / 4;
@@ -97,9 +113,9 @@ __device__ __forceinline__ void issue_scale_tile(const GemmP& p, int m0, int n0,
       cut = lim_w < SBW / 4 && e % (SBW / 4) >= lim_w;
       src = p.ws + (int64_t)r * p.ldws + kt * SBW + (e % (SBW / 4)) * 4;
     } else {
-      src = SBA ? p.as + (int64_t)(m0 < p.M ? m0 : p.M - 1) * p.ldas + kt * SBA : g_zero16;
+      src = SBA ? p.as + (int64_t)(m0 < p.M ? m0 : p.M - 1) * p.ldas + kt * SBA : zsrc;
     }
-    src = (zero || cut) ? g_zero16 : src;
+    src = (zero || cut) ? zsrc : src;
     __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(region + slot0 * 4), 4, 0, 0);
   }
 }
