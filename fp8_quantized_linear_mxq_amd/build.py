@@ -1,4 +1,5 @@
-"""Build libmxq.so in-tree with hipcc for gfx950.
+"""Build libmxq.so (and the matrix-core probe library) in-tree with hipcc
+for gfx950.
 
 Usage: python -m fp8_quantized_linear_mxq_amd.build  (or build() from Python).
 Objects go to _build/ at the repository root; the shared library is written
@@ -17,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxq.so")
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_probe.hip")
+PROBE_LIB = os.path.join(PKG, "probe", "libmxq_probe.so")
 SOURCES = ["api.cpp", "quantize.hip", "lowrank.hip", "gemm_mx.hip", "gemm_dq.hip", "gemm_dqp.hip",
            "mse.hip", "lowrank_split.hip"]
 ARCH = "gfx950"
@@ -56,8 +59,15 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the matrix-core probes: a separate library, never loaded by the layer
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *_flags(), "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
