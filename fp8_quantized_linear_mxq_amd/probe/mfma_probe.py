@@ -1,6 +1,6 @@
 """Matrix-core probes behind two design decisions (GPU only):
 
-  python -m fp8_quantized_linear_mxq_amd.probe.mfma_probe [--rate-only|--sum-only]
+  python -m fp8_quantized_linear_mxq_amd.probe.mfma_probe [--rate-only|--sum-only|--layout|--gemm-data]
 
 1. Summation: single MFMAs on operands whose exact results the host computes
    with rationals -- random finite codes and block scales, and a
@@ -13,6 +13,8 @@
 2. Rate: independent MFMAs from registers on one workgroup per compute unit
    (4 or 8 waves), random or all-zero operands; TFLOP/s against the
    published dense peaks (MXFP4 10.1, FP8 5.0, bf16 2.5 PFLOP/s).
+3. GEMM operand data (--gemm-data): the library's MXFP4 GEMM timed on
+   random, sparse and all-zero codes.
 Prints one JSON line per measurement.
 """
 from __future__ import annotations
@@ -328,15 +330,87 @@ def rate(lib, torch, iters=4000):
     return out
 
 
+def gemm_data(torch, shapes=((4096, 3072, 3072, 0), (4096, 3072, 3072, 32), (4096, 12288, 3072, 0)), rounds=3):
+    """The library's MXFP4 GEMM on operands whose codes are random, all
+    zero, or zero except 1 in 8 bytes: same instructions, same addresses,
+    different switching activity (block scales random in every case).
+    Median us per launch over HIP-graph replays across 8 buffer sets."""
+    import statistics
+    import fp8_quantized_linear_mxq_amd as mxq
+    from fp8_quantized_linear_mxq_amd import _lib
+    out = []
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+
+    def operand(rows, cols, mode):
+        q = _lib.empty_qtensor(mxq.MXFP4, rows, cols, "cuda")
+        codes = torch.randint(0, 256, q.codes.shape, dtype=torch.uint8, device="cuda", generator=gen)
+        if mode == "zero":
+            codes.zero_()
+        elif mode == "sparse":
+            keep = torch.rand(q.codes.shape, device="cuda", generator=gen) < 0.125
+            codes = torch.where(keep, codes, torch.zeros_like(codes))
+        q.codes.copy_(codes)
+        q.scales.copy_(torch.randint(118, 127, q.scales.shape, dtype=torch.uint8, device="cuda", generator=gen))
+        return q
+
+    for m, n, k, r in shapes:
+        for mode in ("random", "sparse", "zero"):
+            sets = []
+            for _ in range(8):
+                a, w = operand(m, k, mode), operand(n, k, mode)
+                u = torch.randn((m, max(r, 1)), device="cuda", generator=gen) if r else None
+                l2t = (torch.randn((n, r), device="cuda", generator=gen) * 0.02).to(torch.bfloat16) if r else None
+                y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+                sets.append((a, w, u, l2t, y))
+            stream = torch.cuda.Stream()
+
+            def call(s):
+                a, w, u, l2t, y = s
+                mxq.gemm(a, w, u=u, l2t=l2t, out=y, workspace=False)
+            with torch.cuda.stream(stream):
+                for s in sets:
+                    call(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for s in sets:
+                    call(s)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                for _ in range(40):
+                    g.replay()
+            res = []
+            for _ in range(rounds):
+                with torch.cuda.stream(stream):
+                    e0.record(stream)
+                    for _ in range(30):
+                        g.replay()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                res.append(e0.elapsed_time(e1) * 1e3 / (30 * len(sets)))
+            us = statistics.median(res)
+            fl = 2.0 * m * n * k + 2.0 * m * n * r
+            rec = {"probe": "gemm_data", "shape": [m, k, n], "rank": r, "codes": mode,
+                   "us_per_launch": round(us, 2), "TFLOPs": round(fl / us / 1e6, 1)}
+            out.append(rec)
+            print(json.dumps(rec), flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--rate-only", action="store_true")
     ap.add_argument("--sum-only", action="store_true")
     ap.add_argument("--layout", action="store_true")
+    ap.add_argument("--gemm-data", action="store_true")
     args = ap.parse_args()
     import torch
     assert torch.cuda.is_available(), "the probes need a GPU"
     lib = _lib()
+    if args.gemm_data:
+        gemm_data(torch)
+        return
     if args.layout:
         for kind in (0, 2, 1):
             res = layout(lib, torch, kind)
