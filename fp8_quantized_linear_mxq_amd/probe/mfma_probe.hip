@@ -6,7 +6,9 @@
 //    kinds the GEMM routes use;
 //  * probe_mfma_sum: one MFMA of a given kind on caller-given operands and
 //    per-lane block scales, so that the host can compare every output with
-//    the exact sum of its products.
+//    the exact sum of its products;
+//  * probe_cvt_scale: the scaled E2M1 converts with arbitrary fp32 scales
+//    (whether a non-power-of-two scale is applied exactly).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -101,9 +103,66 @@ __global__ __launch_bounds__(64) void mfma_sum_kernel(const int* a_ops, const in
   for (int q = 0; q < 16; ++q) d[l * 16 + q] = acc[q];
 }
 
+// Thread i converts all 16 E2M1 codes with scale scales[i] through one of
+// the scaled converts (KIND 0: pk_f16_fp4, 1: pk_bf16_fp4, 2: pk_f32_fp4)
+// and writes the 16 results' bits (16-bit results zero-extended) to
+// out[16 i .. 16 i + 15].
+template <int KIND, int SEL>
+__device__ __forceinline__ void cvt_pair(uint32_t word, float s, uint32_t& lo, uint32_t& hi) {
+  typedef _Float16 v2h_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 v2b_t __attribute__((ext_vector_type(2)));
+  typedef float v2f_t __attribute__((ext_vector_type(2)));
+  if constexpr (KIND == 0) {
+    const v2h_t r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(word, s, SEL);
+    lo = __builtin_bit_cast(uint16_t, r.x); hi = __builtin_bit_cast(uint16_t, r.y);
+  } else if constexpr (KIND == 1) {
+    const v2b_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, SEL);
+    lo = __builtin_bit_cast(uint16_t, r.x); hi = __builtin_bit_cast(uint16_t, r.y);
+  } else {
+    const v2f_t r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, s, SEL);
+    lo = __float_as_uint(r.x); hi = __float_as_uint(r.y);
+  }
+}
+
+// Thread i converts all 16 E2M1 codes with scale scales[i] through one of
+// the scaled converts (KIND 0: pk_f16_fp4, 1: pk_bf16_fp4, 2: pk_f32_fp4)
+// and writes the 16 results' bits (16-bit results zero-extended) to
+// out[16 i .. 16 i + 15].
+template <int KIND>
+__global__ __launch_bounds__(256) void cvt_scale_kernel(const float* scales, int n, uint32_t* out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float s = scales[i];
+  const uint32_t words[2] = {0x76543210u, 0xFEDCBA98u};
+  uint32_t r[16];
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    cvt_pair<KIND, 0>(words[w], s, r[8 * w + 0], r[8 * w + 1]);
+    cvt_pair<KIND, 1>(words[w], s, r[8 * w + 2], r[8 * w + 3]);
+    cvt_pair<KIND, 2>(words[w], s, r[8 * w + 4], r[8 * w + 5]);
+    cvt_pair<KIND, 3>(words[w], s, r[8 * w + 6], r[8 * w + 7]);
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) out[16 * i + k] = r[k];
+}
+
 }  // namespace
 
 extern "C" {
+
+// The scaled E2M1 converts on every code for n caller-given fp32 scales
+// (device pointers; out: n * 16 uint32).  kind 0: to f16, 1: to bf16,
+// 2: to f32.  Returns a hipError_t.
+int probe_cvt_scale(int kind, const float* scales, int n, uint32_t* out, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!scales || !out || n < 1) return (int)hipErrorInvalidValue;
+  const dim3 g((n + 255) / 256), t(256);
+  if (kind == 0) cvt_scale_kernel<0><<<g, t, 0, s>>>(scales, n, out);
+  else if (kind == 1) cvt_scale_kernel<1><<<g, t, 0, s>>>(scales, n, out);
+  else if (kind == 2) cvt_scale_kernel<2><<<g, t, 0, s>>>(scales, n, out);
+  else return (int)hipErrorInvalidValue;
+  return (int)hipGetLastError();
+}
 
 // Enqueues `blocks` workgroups of `waves` waves, each wave issuing
 // iters * 8 independent MFMAs of `kind` (0 FP4 scaled, 1 FP8 x FP4 scaled,

@@ -44,6 +44,7 @@ def _lib():
     lib = C.CDLL(LIB)
     lib.probe_mfma_rate.argtypes = [C.c_int] * 5 + [C.c_void_p, C.c_void_p]
     lib.probe_mfma_sum.argtypes = [C.c_int] + [C.c_void_p] * 6
+    lib.probe_cvt_scale.argtypes = [C.c_int, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p]
     return lib
 
 
@@ -398,16 +399,64 @@ def gemm_data(torch, shapes=((4096, 3072, 3072, 0), (4096, 3072, 3072, 32), (409
     return out
 
 
+def cvt_scale(lib, torch):
+    """Each scaled E2M1 convert (to f16, bf16, f32) on all 16 codes times
+    every positive finite E4M3 value, and times E4M3 values times a
+    non-power-of-two fp32 g: the results against the exact products (which
+    f16 and bf16 hold exactly for E4M3 scales: at most 6 significant bits,
+    magnitudes 2**-10 .. 2688)."""
+    vals = [float(e4m3(c)) for c in range(1, 0x7F)]
+    scales = vals + [v * 1.1904761791229248 for v in vals[:40]]
+    sd = torch.tensor(scales, dtype=torch.float32, device="cuda")
+    out = []
+    for kind, name in ((0, "pk_f16_fp4"), (1, "pk_bf16_fp4"), (2, "pk_f32_fp4")):
+        res = torch.zeros((len(scales) * 16,), dtype=torch.int32, device="cuda")
+        st = lib.probe_cvt_scale(kind, C.c_void_p(sd.data_ptr()), len(scales), C.c_void_p(res.data_ptr()),
+                                 C.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert st == 0, st
+        torch.cuda.synchronize()
+        bits = res.cpu().numpy().astype(np.uint32)
+        bad_e4m3, bad_g, worst = 0, 0, 0.0
+        for i, s in enumerate(scales):
+            s32 = float(np.float32(s))
+            for c in range(16):
+                want = float(e2m1(c)) * s32
+                b = int(bits[16 * i + c])
+                if kind == 0:
+                    got = float(np.array([b], dtype=np.uint16).view(np.float16)[0])
+                elif kind == 1:
+                    got = float(np.array([b << 16], dtype=np.uint32).view(np.float32)[0])
+                else:
+                    got = float(np.array([b], dtype=np.uint32).view(np.float32)[0])
+                if got != want:
+                    if i < len(vals):
+                        bad_e4m3 += 1
+                    else:
+                        bad_g += 1
+                    if want:
+                        worst = max(worst, abs(got - want) / abs(want))
+        rec = {"probe": "cvt_scale", "convert": name, "e4m3_scales": len(vals),
+               "mismatches_e4m3_scales": bad_e4m3, "g_scaled_scales": len(scales) - len(vals),
+               "mismatches_g_scaled": bad_g, "worst_rel_err": worst}
+        out.append(rec)
+        print(json.dumps(rec), flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--rate-only", action="store_true")
     ap.add_argument("--sum-only", action="store_true")
     ap.add_argument("--layout", action="store_true")
     ap.add_argument("--gemm-data", action="store_true")
+    ap.add_argument("--cvt", action="store_true")
     args = ap.parse_args()
     import torch
     assert torch.cuda.is_available(), "the probes need a GPU"
     lib = _lib()
+    if args.cvt:
+        cvt_scale(lib, torch)
+        return
     if args.gemm_data:
         gemm_data(torch)
         return
