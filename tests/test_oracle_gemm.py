@@ -83,3 +83,28 @@ def test_tolerance_covers_bf16_subnormal_rounding():
     # a normal value's rounding stays within 2**-8 |y|
     y = np.array([[1.0 + 2 ** -8]])
     assert abs(og.round_to_bf16(y) - y)[0, 0] <= 2 ** -8 * y[0, 0]
+
+
+def test_lowrank_terms_against_exact_rationals():
+    """u = x L1 and y = a w^T + u L2 + bias on dyadic inputs, against sums of
+    Fractions written out element by element (every float64 partial sum is
+    exact here, so the oracle must match to the bit); a transposed operand or
+    a dropped term fails."""
+    from fractions import Fraction as F
+    rng = np.random.default_rng(9)
+    m, k, r, n = 3, 8, 2, 4
+    dy = lambda *s: rng.integers(-8, 9, size=s) * 2.0 ** rng.integers(-4, 4, size=s)
+    x, l1, a, w, l2, b = dy(m, k), dy(k, r), dy(m, k), dy(n, k), dy(r, n), dy(n)
+    u = og.lowrank_down(x, l1)
+    for i in range(m):
+        for j in range(r):
+            assert u[i, j] == float(sum(F(x[i, t]) * F(l1[t, j]) for t in range(k)))
+    y = og.linear(a, w, 1.0, u, l2, b)
+    for i in range(m):
+        for j in range(n):
+            want = (sum(F(a[i, t]) * F(w[j, t]) for t in range(k))
+                    + sum(F(u[i, q]) * F(l2[q, j]) for q in range(r)) + F(b[j]))
+            assert y[i, j] == float(want)
+    # planted slips: L2 used transposed-by-index, or the bias dropped
+    assert not np.array_equal(og.linear(a, w, 1.0, u, l2, b), og.linear(a, w, 1.0, u, l2))
+    assert not np.array_equal(y, og.linear(a, w, 1.0, u, l2[::-1], b))
