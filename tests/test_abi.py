@@ -149,3 +149,43 @@ def test_status_codes_and_no_device(lib):
     st = lib.mxq_gemm(C.byref(a), C.byref(w), None, None, 0, None, 0, None, vp(1 << 27), 8, 8,
                       None, 0, None)
     assert st == 6
+
+
+def test_validation_of_weight_preparation_entry_points(lib):
+    """mxq_quantize_mse, mxq_lowrank_split and mxq_quantize_noalloc reject
+    bad arguments before any device work (stand-in pointers, never read)."""
+    vp = C.c_void_p
+    # MSE scales: MXFP8 is a known format without MSE scales, K not a
+    # multiple of 32, misaligned input, NVFP4 without its workspace, empty
+    q8 = _lib.QTensorC(2, 0, 4, 64, vp(4096), 64, vp(8192), 4, None)
+    assert lib.mxq_quantize_mse(vp(16), 1, 4, 64, 64, C.byref(q8), None, 0, None) == 2
+    q99 = _lib.QTensorC(99, 0, 4, 64, vp(4096), 32, vp(8192), 4, None)
+    assert lib.mxq_quantize_mse(vp(16), 1, 4, 64, 64, C.byref(q99), None, 0, None) == 1
+    q48 = _lib.QTensorC(1, 0, 4, 48, vp(4096), 32, vp(8192), 4, None)
+    assert lib.mxq_quantize_mse(vp(16), 1, 4, 48, 48, C.byref(q48), None, 0, None) == 4
+    q4 = _lib.QTensorC(1, 0, 4, 64, vp(4096), 32, vp(8192), 4, None)
+    assert lib.mxq_quantize_mse(vp(18), 1, 4, 64, 64, C.byref(q4), None, 0, None) == 3
+    assert lib.mxq_quantize_mse(vp(16), 7, 4, 64, 64, C.byref(q4), None, 0, None) == 1
+    qn = _lib.QTensorC(3, 0, 4, 64, vp(4096), 32, vp(8192), 4, vp(12288))
+    assert lib.mxq_quantize_mse(vp(16), 1, 4, 64, 64, C.byref(qn), None, 0, None) == 5
+    q0 = _lib.QTensorC(1, 0, 0, 64, None, 32, None, 4, None)
+    assert lib.mxq_quantize_mse(None, 1, 0, 64, 64, C.byref(q0), None, 0, None) == 0
+    # SVD split: rank 0 or above 128, rank above min(n, k), null factor,
+    # misaligned residual, workspace missing or too small
+    split = lib.mxq_lowrank_split
+    args = lambda **o: dict(dict(w=vp(1 << 20), n=64, k=96, ldw=96, rank=8, iters=0, l1t=vp(1 << 21),
+                                 l2t=vp(1 << 22), resid=vp(1 << 23), ld_resid=96, sigma=None,
+                                 ws=vp(1 << 24), wsb=1 << 30, st=None), **o)
+    call = lambda a: split(a["w"], a["n"], a["k"], a["ldw"], a["rank"], a["iters"], a["l1t"], a["l2t"],
+                           a["resid"], a["ld_resid"], a["sigma"], a["ws"], a["wsb"], a["st"])
+    assert call(args(rank=0)) == 1
+    assert call(args(rank=144)) == 1
+    assert call(args(rank=80, k=64, ldw=64, ld_resid=64)) == 4
+    assert call(args(l1t=None)) == 1
+    assert call(args(resid=vp((1 << 23) + 2))) == 3
+    assert call(args(ws=None)) == 5
+    need = _lib.workspace_size(_lib.OP_LOWRANK_SPLIT, 64, 96, 8)
+    assert need > 0 and call(args(wsb=need - 1)) == 5
+    # the allocation-free quantize validates like mxq_quantize
+    assert lib.mxq_quantize_noalloc(None, 1, 4, 64, 64, 0, None, None, 0, None, 0, C.byref(q4), None) == 1
+    assert lib.mxq_quantize_noalloc(vp(16), 1, 4, 48, 48, 0, None, None, 0, None, 0, C.byref(q48), None) == 4
