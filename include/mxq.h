@@ -66,8 +66,10 @@
  *    on that device returns MXQ_ERR_NONFINITE (and clears the flag) instead
  *    of running.  Debug mode reads the flag synchronously at every such
  *    call, so it synchronizes the device and cannot be graph-captured.
- *  - Apart from that one debug flag per device the library keeps no state;
- *    calls on distinct streams are independent.
+ *  - Apart from that debug flag and mxq_quantize_noalloc's scratch array
+ *    (one of each per device) the library keeps no state; calls on distinct
+ *    streams are independent, except mxq_quantize_noalloc calls that
+ *    overlap in time on one device (they share its scratch array).
  */
 #ifndef MXQ_H
 #define MXQ_H
