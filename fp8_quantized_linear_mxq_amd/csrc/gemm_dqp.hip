@@ -14,9 +14,13 @@
 // tensor scales multiply the accumulator in the epilogue.
 //
 // Organisation (the same pipeline as the MXFP4 kernel):
-//  * workgroup tile (32*TM*WGM) x (64*TN), 2*WGM waves in a WGM x 2 grid
-//    (four, or eight for 256-row tiles), each wave (32*TM) x (32*TN): every
-//    dequantized fragment feeds TN (activation) or TM (weight) MFMAs;
+//  * workgroup tile (32*TM*WGM) x (32*TN*WGN), WGM*WGN waves in a WGM x WGN
+//    grid (four, or eight for 256-row tiles), each wave (32*TM) x (32*TN):
+//    every dequantized fragment feeds TN (activation) or TM (weight) MFMAs.
+//    NVFP4 weights against other activations take tall wave tiles (TM > TN):
+//    their fragment costs four converts, eight multiplies and four packs
+//    against the activation's four converts, so each one should feed more
+//    MFMAs;
 //  * raw code and scale tiles (4-bit codes are a quarter, 8-bit codes half
 //    the bytes of 16-bit tiles) stream into a 3-stage LDS ring with direct
 //    global->LDS loads two K-tiles ahead of the MFMAs;
@@ -143,12 +147,12 @@ __device__ __forceinline__ uint4 dq(const uint32_t* raw, int ks, const Scales<K,
   }
 }
 
-template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR, bool CONV>
+template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR, bool CONV, int WGN>
 __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
   const GemmP& p = dp.g;
   constexpr bool FP16 = (AK == K_NV && WK == K_NV);
-  constexpr int NW = 2 * WGM;   // waves: WGM (rows) x 2 (columns)
-  constexpr int TBM = 32 * TM * WGM, TBN = 64 * TN;
+  constexpr int NW = WGM * WGN;   // waves: WGM (rows) x WGN (columns)
+  constexpr int TBM = 32 * TM * WGM, TBN = 32 * TN * WGN;
   constexpr int A_RB = row_bytes<AK>(), W_RB = row_bytes<WK>();
   constexpr int A_CH = A_RB / 16, W_CH = W_RB / 16;
   constexpr int SBA = scale_bytes<AK>(), SBW = scale_bytes<WK>();
@@ -170,7 +174,7 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, dp.gm, tm, tn);
   const int m0 = tm * TBM, n0 = tn * TBN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int l32 = lane & 31, half = lane >> 5;
   const int KT = p.K / BK;
 
@@ -413,33 +417,55 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
   epilogue_tr<LR, TM, TN>(p, acc, alpha, m0 + wm * 32 * TM, n0 + wn * 32 * TN, lane, region);
 }
 
+// Tall wave tiles where the weight fragment is the dearer one to dequantize
+// (NVFP4 weights against MX or bf16 activations): 128x128 workgroup tiles as
+// 1 x 4 waves of 128 x 32 instead of 2 x 2 of 64 x 64 (0.25 weight and one
+// activation fragment per MFMA instead of 0.5 and 0.5), 256x256 as 2 x 4
+// waves of 128 x 64 instead of 4 x 2 of 64 x 128.
+template <int AK, int WK>
+constexpr bool tall_waves() { return WK == K_NV && AK != K_NV; }
+
 // Slabbed tiles run two workgroups per CU, except with bf16 activations,
 // whose three LDS stages take 123 KB.
-template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR>
-__global__ __launch_bounds__(128 * WGM, (SLAB && AK != K_BF) ? 2 : 1) void gemm_dqp_kernel(
+template <int AK, int WK, int TM, int TN, int WGM, bool SLAB, bool LR, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, (SLAB && AK != K_BF) ? 2 : 1) void gemm_dqp_kernel(
     DqpParams dp) {
-  dqp_body<AK, WK, TM, TN, WGM, SLAB, LR, false>(dp);
+  dqp_body<AK, WK, TM, TN, WGM, SLAB, LR, false, WGN>(dp);
 }
 
 // The same GEMM with the activation operand read as the implicit im2col of a
 // 3x3 convolution (128x128 tiles, two workgroups per compute unit).
 template <int AK, int WK, bool SLAB>
 __global__ __launch_bounds__(256, 2) void conv_dqp_kernel(DqpParams dp) {
-  dqp_body<AK, WK, 2, 2, 2, SLAB, false, true>(dp);
+  if constexpr (tall_waves<AK, WK>()) dqp_body<AK, WK, 4, 1, 1, SLAB, false, true, 4>(dp);
+  else dqp_body<AK, WK, 2, 2, 2, SLAB, false, true, 2>(dp);
 }
 
-template <int AK, int WK, int TM, int TN, bool SLAB, int WGM = 2>
+template <int AK, int WK, int TM, int TN, bool SLAB, int WGM = 2, int WGN = 2>
 hipError_t launch_cfg(bool lr, DqpParams dp, hipStream_t s) {
   dp.g.tiles_m = (dp.g.M + 32 * TM * WGM - 1) / (32 * TM * WGM);
-  dp.g.tiles_n = (dp.g.N + 64 * TN - 1) / (64 * TN);
+  dp.g.tiles_n = (dp.g.N + 32 * TN * WGN - 1) / (32 * TN * WGN);
   const int tiles = dp.g.tiles_m * dp.g.tiles_n;
   // tile-rows per group: one XCD's share (tiles / 8) as a near-square block
   dp.gm = 1;
   while (dp.gm * 2 <= dp.g.tiles_m && dp.gm * 2 * dp.gm * 2 <= (tiles + 7) / 8) dp.gm *= 2;
   const dim3 grid(tiles);
-  if (lr) gemm_dqp_kernel<AK, WK, TM, TN, WGM, SLAB, true><<<grid, 128 * WGM, 0, s>>>(dp);
-  else gemm_dqp_kernel<AK, WK, TM, TN, WGM, SLAB, false><<<grid, 128 * WGM, 0, s>>>(dp);
+  if (lr) gemm_dqp_kernel<AK, WK, TM, TN, WGM, SLAB, true, WGN><<<grid, 64 * WGM * WGN, 0, s>>>(dp);
+  else gemm_dqp_kernel<AK, WK, TM, TN, WGM, SLAB, false, WGN><<<grid, 64 * WGM * WGN, 0, s>>>(dp);
   return hipGetLastError();
+}
+
+// The 128x128 and 256x256 workgroup tiles in the wave layout the pair takes.
+template <int AK, int WK, bool SLAB>
+hipError_t launch_128(bool lr, const DqpParams& dp, hipStream_t s) {
+  if constexpr (tall_waves<AK, WK>()) return launch_cfg<AK, WK, 4, 1, SLAB, 1, 4>(lr, dp, s);
+  else return launch_cfg<AK, WK, 2, 2, SLAB>(lr, dp, s);
+}
+
+template <int AK, int WK>
+hipError_t launch_256(bool lr, const DqpParams& dp, hipStream_t s) {
+  if constexpr (tall_waves<AK, WK>()) return launch_cfg<AK, WK, 4, 2, false, 2, 4>(lr, dp, s);
+  else return launch_cfg<AK, WK, 2, 4, false, 4>(lr, dp, s);
 }
 
 template <int AK, int WK>
@@ -460,7 +486,7 @@ hipError_t launch_tiles(bool lr, const DqpParams& dp, hipStream_t s) {
   const int64_t M = dp.g.M, N = dp.g.N;
   // past 32 K-tiles the fp32 chains are flushed into a second accumulator
   // every kSlab K-tiles, which only the small tile has the registers for
-  if (dp.g.K / BK > 32) return launch_cfg<AK, WK, 2, 2, true>(lr, dp, s);
+  if (dp.g.K / BK > 32) return launch_128<AK, WK, true>(lr, dp, s);
   // Costs in 64x64 output blocks per compute unit over whole rounds of the
   // 256 compute units: the tile that fills them in the fewest rounds per
   // unit of work.  256-row tiles run eight waves (two per SIMD, wave tiles
@@ -477,12 +503,12 @@ hipError_t launch_tiles(bool lr, const DqpParams& dp, hipStream_t s) {
   const int64_t c4 = rounds(256, 256, 1) * 16, c3 = rounds(256, 192, 1) * 12;
   if (dp.g.K / BK < 16) {
     const int64_t c1 = rounds(128, 128, 2) * 8;
-    if (c4 < c1 && c4 <= c3) return launch_cfg<AK, WK, 2, 4, false, 4>(lr, dp, s);
+    if (c4 < c1 && c4 <= c3) return launch_256<AK, WK>(lr, dp, s);
     if (c3 < c1) return launch_cfg<AK, WK, 2, 3, false, 4>(lr, dp, s);
-    return launch_cfg<AK, WK, 2, 2, false>(lr, dp, s);
+    return launch_128<AK, WK, false>(lr, dp, s);
   }
   const int64_t c2 = rounds(256, 128, 1) * 8;
-  if (c4 <= c3 && c4 <= c2) return launch_cfg<AK, WK, 2, 4, false, 4>(lr, dp, s);
+  if (c4 <= c3 && c4 <= c2) return launch_256<AK, WK>(lr, dp, s);
   if (c3 <= c2) return launch_cfg<AK, WK, 2, 3, false, 4>(lr, dp, s);
   return launch_cfg<AK, WK, 4, 2, false>(lr, dp, s);
 }
@@ -496,9 +522,9 @@ hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
     // with NVFP4 weights, whose dequantization is dearer, the taller tile
     // amortizes it over twice the rows and is as fast.
     if (dp.g.cv_c > 0) return hipErrorInvalidValue;
-    if (dp.g.K / BK > 32) return launch_cfg<AK, WK, 2, 2, true>(lr, dp, s);
+    if (dp.g.K / BK > 32) return launch_128<AK, WK, true>(lr, dp, s);
     if constexpr (WK == K_MX4) return launch_cfg<AK, WK, 1, 2, false>(lr, dp, s);
-    else return launch_cfg<AK, WK, 2, 2, false>(lr, dp, s);
+    else return launch_128<AK, WK, false>(lr, dp, s);
   } else {
     if (dp.g.cv_c > 0) return launch_conv<AK, WK>(dp, s);
     return launch_tiles<AK, WK>(lr, dp, s);

@@ -150,6 +150,34 @@ def test_gemm_dq_tiles(fa, fw, m, n, k):
     gu.say(f"  worst err/tol {ratio:.3g}")
 
 
+@pytest.mark.parametrize("fa,fw", [("MXFP8", "NVFP4"), ("MXFP4", "NVFP4"), ("MXFP8", "MXFP4")])
+def test_gemm_dq_wide_tiles_lowrank(fa, fw):
+    """256x256 workgroup tiles (eight waves; 128x64 wave tiles for NVFP4 weights against MX
+    activations, 64x128 otherwise) with the low-rank branch and bias in the epilogue; ragged
+    M and N; output rows checked on a sample that includes both tile rows of a workgroup."""
+    import fp8_quantized_linear_mxq_amd as mxq
+    m, n, k = 4000, 4000, 2048
+    gu.say(f"gemm {fa}x{fw} 256x256 tiles + low rank M={m} N={n} K={k}")
+    qa, qw = _operands(m, n, k, fa, fw, seed=17 + len(fa + fw))
+    rng = np.random.default_rng(23)
+    r = 32
+    u = (rng.standard_normal((m, r)) * 4).astype(np.float32)
+    l2 = wl.bf16_to_f32(wl.f32_to_bf16_bits(rng.normal(0, 0.02, (r, n)).astype(np.float32)))
+    bias = wl.bf16_to_f32(wl.f32_to_bf16_bits(rng.normal(0, 1, n).astype(np.float32)))
+    y = mxq.gemm(gu.qtensor_from_oracle(qa, m, k), gu.qtensor_from_oracle(qw, n, k),
+                 u=gu.to_dev_f32(u),
+                 l2t=gu.to_dev_bf16(wl.f32_to_bf16_bits(np.ascontiguousarray(l2.T))),
+                 bias=gu.to_dev_bf16(wl.f32_to_bf16_bits(bias)))
+    rows = np.unique(np.concatenate([rng.choice(m, 80, replace=False),
+                                     [0, 127, 128, 255, 256, 3839, 3840, m - 1]]))
+    alpha = gu.alpha_of(qa, qw)
+    a_deq = np.hstack([gu.dequant_a_for_gemm(qa)[rows], u[rows].astype(np.float64)])
+    w_deq = np.hstack([gu.dequant_w_for_gemm(qw), l2.T.astype(np.float64) / alpha])
+    ratio = gu.check_gemm(y, a_deq, w_deq, alpha, bias=bias, rows=rows,
+                          tag=f"{fa}x{fw} 256x256 lr")
+    gu.say(f"  worst err/tol {ratio:.3g}")
+
+
 @pytest.mark.parametrize("fa", ["MXFP8", "NVFP4", "MXFP4"])
 def test_int4_split_k(fa):
     """Narrow INT4 weight groups (few output tiles) split K into fp32 partial
