@@ -17,10 +17,13 @@
 //  * workgroup tile (32*TM*WGM) x (32*TN*WGN), WGM*WGN waves in a WGM x WGN
 //    grid (four, or eight for 256-row tiles), each wave (32*TM) x (32*TN):
 //    every dequantized fragment feeds TN (activation) or TM (weight) MFMAs.
-//    NVFP4 weights against other activations take tall wave tiles (TM > TN):
-//    their fragment costs four converts, eight multiplies and four packs
-//    against the activation's four converts, so each one should feed more
-//    MFMAs;
+//    An NVFP4 fragment dequantized to bf16 costs four converts, eight
+//    multiplies and four packs against an MX fragment's four converts (a
+//    bf16 activation fragment costs none), so the operand that is dearer to
+//    dequantize gets the longer side of the wave tile: tall tiles (TM > TN)
+//    for NVFP4 weights against MX or bf16 activations and for MXFP4 weights
+//    against bf16 activations, wide ones for NVFP4 activations against
+//    MXFP4 weights;
 //  * raw code and scale tiles (4-bit codes are a quarter, 8-bit codes half
 //    the bytes of 16-bit tiles) stream into a 3-stage LDS ring with direct
 //    global->LDS loads two K-tiles ahead of the MFMAs;
@@ -421,9 +424,14 @@ __device__ __forceinline__ void dqp_body(const DqpParams& dp) {
 // (NVFP4 weights against MX or bf16 activations): 128x128 workgroup tiles as
 // 1 x 4 waves of 128 x 32 instead of 2 x 2 of 64 x 64 (0.25 weight and one
 // activation fragment per MFMA instead of 0.5 and 0.5), 256x256 as 2 x 4
-// waves of 128 x 64 instead of 4 x 2 of 64 x 128.
+// waves of 128 x 64 instead of 4 x 2 of 64 x 128.  Wide ones where the
+// activation fragment is (NVFP4 activations, MXFP4 weights): 128x128 as
+// 4 x 1 waves of 32 x 128 (the 256x256 tile's 64 x 128 waves are wide
+// already).
 template <int AK, int WK>
 constexpr bool tall_waves() { return WK == K_NV && AK != K_NV; }
+template <int AK, int WK>
+constexpr bool wide_waves() { return AK == K_NV && WK == K_MX4; }
 
 // Slabbed tiles run two workgroups per CU, except with bf16 activations,
 // whose three LDS stages take 123 KB.
@@ -438,6 +446,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, (SLAB && AK != K_BF) ? 2 : 1) void 
 template <int AK, int WK, bool SLAB>
 __global__ __launch_bounds__(256, 2) void conv_dqp_kernel(DqpParams dp) {
   if constexpr (tall_waves<AK, WK>()) dqp_body<AK, WK, 4, 1, 1, SLAB, false, true, 4>(dp);
+  else if constexpr (wide_waves<AK, WK>()) dqp_body<AK, WK, 1, 4, 4, SLAB, false, true, 1>(dp);
   else dqp_body<AK, WK, 2, 2, 2, SLAB, false, true, 2>(dp);
 }
 
@@ -459,6 +468,7 @@ hipError_t launch_cfg(bool lr, DqpParams dp, hipStream_t s) {
 template <int AK, int WK, bool SLAB>
 hipError_t launch_128(bool lr, const DqpParams& dp, hipStream_t s) {
   if constexpr (tall_waves<AK, WK>()) return launch_cfg<AK, WK, 4, 1, SLAB, 1, 4>(lr, dp, s);
+  else if constexpr (wide_waves<AK, WK>()) return launch_cfg<AK, WK, 1, 4, SLAB, 4, 1>(lr, dp, s);
   else return launch_cfg<AK, WK, 2, 2, SLAB>(lr, dp, s);
 }
 
@@ -518,12 +528,13 @@ hipError_t launch_pair(bool lr, const DqpParams& dp, hipStream_t s) {
   if constexpr (AK == K_BF) {
     // 16-bit activation tiles are 256 bytes a row: the 128x128 tile's three
     // stages take 123 KB (one workgroup per CU).  With MXFP4 weights 64x128
-    // tiles (75 KB, two per CU) are faster (4096x1152x4608: 84 -> 76 us);
-    // with NVFP4 weights, whose dequantization is dearer, the taller tile
-    // amortizes it over twice the rows and is as fast.
+    // tiles (75 KB, two per CU; 1 x 4 waves of 64 x 32, since only the
+    // weight fragments need converting) are faster (4096x1152x4608: 84 -> 76
+    // us with 2 x 2 waves); with NVFP4 weights, whose dequantization is
+    // dearer, the taller tile amortizes it over twice the rows and is as fast.
     if (dp.g.cv_c > 0) return hipErrorInvalidValue;
     if (dp.g.K / BK > 32) return launch_128<AK, WK, true>(lr, dp, s);
-    if constexpr (WK == K_MX4) return launch_cfg<AK, WK, 1, 2, false>(lr, dp, s);
+    if constexpr (WK == K_MX4) return launch_cfg<AK, WK, 2, 1, false, 1, 4>(lr, dp, s);
     else return launch_128<AK, WK, false>(lr, dp, s);
   } else {
     if (dp.g.cv_c > 0) return launch_conv<AK, WK>(dp, s);
