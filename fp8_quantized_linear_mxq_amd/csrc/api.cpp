@@ -69,6 +69,14 @@ bool debug_checks() {
   return e && e[0] == '1' && e[1] == 0;
 }
 
+// MXQ_NVFP4_TWO_PASS=1 (read at every call) makes the dynamic NVFP4
+// quantize take its two-pass kernels (an amax pass, then the quantize pass)
+// even where the one-pass kernel fits; both give identical results.
+bool nvfp4_two_pass() {
+  const char* e = std::getenv("MXQ_NVFP4_TWO_PASS");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
 // Run once a call has passed validation and is about to enqueue work: a
 // usable device, and in debug mode the non-finite flag a previous call may
 // have set (read and cleared synchronously).  *dbg receives the flag's
@@ -218,6 +226,7 @@ static mxq_status quantize_impl(const void* x, int32_t dtype, int64_t rows, int6
   a.static_tensor_scale = static_tensor_scale;
   a.partials = static_cast<float*>(workspace);
   a.dbg = dbg;
+  a.nv_two_pass = nvfp4_two_pass();
   LoraDownArgs l;
   a.lr = nullptr;
   if (lr_rank > 0) {

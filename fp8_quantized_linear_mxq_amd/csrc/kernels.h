@@ -31,6 +31,7 @@ struct QuantizeArgs {
   float* partials;                  // NVFP4 dynamic: workspace
   const LoraDownArgs* lr;           // optional low-rank down projection (bf16 x)
   unsigned* dbg;                    // debug checks: non-finite flag, else null
+  bool nv_two_pass;                 // dynamic NVFP4: skip the one-pass kernel
 };
 
 constexpr int kAmaxPartials = 1024;  // NVFP4 phase-1 grid (workspace floats)

@@ -16,6 +16,7 @@
 #include <atomic>
 
 #include "device_common.h"
+#include "grid_max.h"
 #include "kernels.h"
 
 namespace mxq {
@@ -411,6 +412,80 @@ __global__ __launch_bounds__(kThreads) void amax32_kernel(QParams p, float* part
   }
 }
 
+// One-pass NVFP4 with the dynamic tensor scale.  The tensor scale depends on
+// the amax of the whole (rotated) tensor, which the two-pass form gets by
+// reading x twice.  Here every lane keeps its J rotated 32-blocks in
+// registers; the workgroups' maxima meet in a device-wide maximum
+// (grid_max.h) that every workgroup waits for, and the blocks are encoded
+// from the registers, so x is read once.  The wait needs every workgroup
+// resident at once: the host sizes the grid from the kernel's occupancy on
+// this device (the two-pass kernels take inputs that do not fit).  A call
+// whose grid could not become resident within about a second (other work
+// holding the compute units) writes a NaN tensor scale.  Consecutive calls
+// take different barrier slots of a small ring; calls ordered on one stream
+// reuse them safely.
+constexpr int kNvSlots = 16;
+__device__ GridMaxSlot g_nvslot[kNvSlots];
+
+template <int DT, int HAD, int J>
+__global__ __launch_bounds__(kThreads) void nvfp4_onepass_kernel(QParams p, uint32_t bpr,
+                                                                 uint32_t nblk, int slot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t b0 = blockIdx.x * (kThreads * J) + threadIdx.x;
+  float v[J][4][8];
+  uint32_t rows[J], cols[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    // lanes past the end work on a clamped block (the 128-point rotation
+    // exchanges lanes) and neither count nor store it
+    const uint32_t b = b0 + j * kThreads;
+    const uint32_t bb = b < nblk ? b : nblk - 1;
+    rows[j] = bb / bpr;
+    cols[j] = (bb - rows[j] * bpr) * 32;
+    load32<DT>(p, rows[j], cols[j], v[j]);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    check_finite<32>(&v[j][0][0], p.dbg);
+    if constexpr (HAD > 0) hadamard32<HAD>(v[j], lane);
+    if (b0 + j * kThreads < nblk) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][k][i]));
+    }
+  }
+  __shared__ float red[kThreads / 64];
+  __shared__ float g_sh;
+  m = group_max<64>(m);
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  if (wave == 0) {
+    float wm = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) wm = fmaxf(wm, red[w]);
+    const float A = grid_max_wave0(&g_nvslot[slot], wm);
+    // g = RN_fp32(A / 2688): the float64 quotient of two float32 values
+    // rounds correctly to float32 (a NaN from a timed-out wait passes on)
+    const float g = (float)((double)A / 2688.0);
+    if (lane == 0) {
+      g_sh = g;
+      if (blockIdx.x == 0 && p.g_out) *p.g_out = g;
+    }
+  }
+  __syncthreads();
+  const float g = g_sh;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    if (b0 + j * kThreads >= nblk) continue;
+    uint32_t code[4][8], sbyte[4];
+    float sfloat[4];
+    encode32<FMT_NVFP4>(v[j], g, code, sbyte, sfloat);
+    store32<FMT_NVFP4>(p, rows[j], cols[j], code, sbyte, sfloat);
+  }
+}
+
 // Quantize fused with the low-rank down projection u = x L1 of the SVDQuant
 // branch (Nunchaku article, "main explanation": the 16-bit low-rank part
 // reads the same unrotated activations).  One workgroup owns 16 rows; its
@@ -734,6 +809,61 @@ hipError_t dispatch_amax(int had, dim3 grid, const QParams& p, float* partials, 
   return hipGetLastError();
 }
 
+// Workgroups of nvfp4_onepass_kernel<DT, HAD, J> the current device holds
+// at once (occupancy x compute units), looked up once per device; 0 when
+// unknown (the caller then takes the two-pass kernels).
+template <int DT, int HAD, int J>
+int onepass_capacity() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+  int c = cache[dev].load(std::memory_order_acquire);
+  if (c == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nvfp4_onepass_kernel<DT, HAD, J>,
+                                                     kThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    c = per_cu > 0 && cus > 0 ? per_cu * cus : -1;
+    cache[dev].store(c, std::memory_order_release);
+  }
+  return c > 0 ? c : 0;
+}
+
+std::atomic<unsigned> g_next_nvslot{0};
+
+// The one-pass kernel with J blocks per lane, if its grid is resident at
+// once on this device; false leaves the work to the two-pass kernels.
+template <int DT, int HAD, int J>
+bool onepass_j(const QParams& p, uint32_t bpr, uint32_t nblk, hipStream_t s, hipError_t* err) {
+  const uint64_t grid = ((uint64_t)nblk + kThreads * J - 1) / (kThreads * J);
+  if (grid > (uint64_t)onepass_capacity<DT, HAD, J>() || grid > (uint64_t)kGridMaxWgs) return false;
+  const int slot = (int)(g_next_nvslot.fetch_add(1u, std::memory_order_relaxed) % kNvSlots);
+  nvfp4_onepass_kernel<DT, HAD, J><<<dim3((unsigned)grid), kThreads, 0, s>>>(p, bpr, nblk, slot);
+  *err = hipGetLastError();
+  return true;
+}
+
+// The fewest blocks per lane (the most workgroups) that fit.
+template <int DT, int HAD>
+bool onepass_had(const QParams& p, uint32_t bpr, uint32_t nblk, hipStream_t s, hipError_t* err) {
+  return onepass_j<DT, HAD, 1>(p, bpr, nblk, s, err) || onepass_j<DT, HAD, 2>(p, bpr, nblk, s, err) ||
+         onepass_j<DT, HAD, 4>(p, bpr, nblk, s, err);
+}
+
+template <int DT>
+bool onepass(int had, const QParams& p, uint32_t bpr, uint32_t nblk, hipStream_t s,
+             hipError_t* err) {
+  switch (had) {
+    case 0: return onepass_had<DT, 0>(p, bpr, nblk, s, err);
+    case 16: return onepass_had<DT, 16>(p, bpr, nblk, s, err);
+    case 32: return onepass_had<DT, 32>(p, bpr, nblk, s, err);
+    case 128: return onepass_had<DT, 128>(p, bpr, nblk, s, err);
+    default: return false;
+  }
+}
+
 }  // namespace
 
 // Scratch of the allocation-free quantize entry point: room for the NVFP4
@@ -805,6 +935,13 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
 
   if (a.fmt == FMT_NVFP4 && a.static_tensor_scale == nullptr) {
+    // one pass over x when the blocks fit in the registers of one resident grid
+    if (!(a.lr && a.lr->rank > 0) && !a.nv_two_pass) {
+      hipError_t e = hipSuccess;
+      const bool done = (a.dtype == DT_BF16) ? onepass<DT_BF16>(a.hadamard_n, p, bpr, nblk, s, &e)
+                                             : onepass<DT_F32>(a.hadamard_n, p, bpr, nblk, s, &e);
+      if (done) return e;
+    }
     uint32_t pb = blocks < (uint32_t)kAmaxPartials ? blocks : (uint32_t)kAmaxPartials;
     p.n_partials = (int)pb;
     hipError_t e = (a.dtype == DT_BF16)

@@ -66,10 +66,14 @@
  *    on that device returns MXQ_ERR_NONFINITE (and clears the flag) instead
  *    of running.  Debug mode reads the flag synchronously at every such
  *    call, so it synchronizes the device and cannot be graph-captured.
- *  - Apart from that debug flag and mxq_quantize_noalloc's scratch array
- *    (one of each per device) the library keeps no state; calls on distinct
- *    streams are independent, except mxq_quantize_noalloc calls that
- *    overlap in time on one device (they share its scratch array).
+ *  - Apart from that debug flag, mxq_quantize_noalloc's scratch array and
+ *    the barrier slots of the one-pass NVFP4 quantize (a ring of 16 per
+ *    device, about 25 KB each, zero at load and left zero by every call) the
+ *    library keeps no state; calls on distinct streams are independent,
+ *    except mxq_quantize_noalloc calls that overlap in time on one device
+ *    (they share its scratch array) and dynamic NVFP4 quantizes: one whose
+ *    grid cannot be resident at once within about a second, because other
+ *    work holds the compute units, writes a NaN tensor scale.
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -142,7 +146,12 @@ typedef struct mxq_qtensor {
  *  hadamard_n  0 (none), 16, 32 or 128; must divide cols.
  *  static_tensor_scale  NVFP4 only: device pointer to a caller-chosen g
  *              (then block scales saturate at 448), or NULL for the dynamic
- *              g computed from this tensor (two passes over x).
+ *              g computed from this tensor: one pass over x when its blocks
+ *              fit in the registers of one resident grid (up to about 16M
+ *              elements, 2048 workgroups; the workgroups meet in a
+ *              device-wide maximum), else two passes (an amax pass, then the
+ *              quantize).  MXQ_NVFP4_TWO_PASS=1 in the environment (read at
+ *              every call) forces the two passes; the results are identical.
  *  lr_l1t, lr_rank, lr_u, ld_u  optional fused low-rank down projection of
  *              the SVDQuant branch (Nunchaku article, main explanation):
  *              u = x L1 on the unrotated bf16 input, with L1^T [lr_rank][cols]
