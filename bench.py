@@ -181,8 +181,14 @@ def make_sets(w: wl.Workload, n_sets: int, mxq, torch, mixed=None, conv="implici
                          dtype=torch.uint8, device="cuda")
         out = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
         u = torch.empty((w.m, w.rank), dtype=torch.float32, device="cuda") if w.rank else None
-        sets.append(dict(x=x, qw=qw, qa=qa, ws=ws, out=out, u=u,
-                         l1t=l1t.clone() if l1t is not None else None,
+        # L1 is part of the weight: where the fused quantize + projection
+        # kernel runs (bf16 x, no rotation), it is packed once here, outside
+        # the timed steps, into the order that kernel reads
+        l1 = l1t.clone() if l1t is not None else None
+        l1p = None
+        if l1 is not None and x.dtype == torch.bfloat16 and w.hadamard == 0 and w.k % 128 == 0:
+            l1p, l1 = mxq.pack_l1t(l1), None
+        sets.append(dict(x=x, qw=qw, qa=qa, ws=ws, out=out, u=u, l1t=l1, l1p=l1p,
                          l2t=l2t.clone() if l2t is not None else None))
     del w0
     torch.cuda.synchronize()
@@ -389,8 +395,8 @@ def main() -> int:
                 raise RuntimeError(f"table routes format {f}; the buffers hold {s['qa'].fmt}")
             mxq.quantize(s["x"], f, out=s["qa"])
         else:
-            mxq.quantize(s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], u=s["u"], out=s["qa"],
-                         workspace=s["ws"])
+            mxq.quantize(s["x"], fa, hadamard=w.hadamard, l1t=s["l1t"], l1p=s["l1p"], u=s["u"],
+                         out=s["qa"], workspace=s["ws"])
 
     def gemm(s):
         if implicit:

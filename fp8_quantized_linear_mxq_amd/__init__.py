@@ -10,6 +10,6 @@ from ._lib import (  # noqa: F401
     OP_QUANTIZE, OP_QUANTIZE_MSE, OP_SELECT,
     MxqError, QTensor,
     act_format_for_step, bf16_operand, lowrank_split, conv3x3_gemm_mixed, empty_qtensor, gemm, gemm_mixed, load,
-    quantize, quantize_mse,
+    pack_l1t, quantize, quantize_mse,
     select_format, storage, workspace_size,
 )

@@ -26,7 +26,7 @@ STATUS = {0: "MXQ_OK", 1: "MXQ_ERR_INVALID_ARG", 2: "MXQ_ERR_UNSUPPORTED",
           6: "MXQ_ERR_NO_DEVICE", 7: "MXQ_ERR_LAUNCH", 8: "MXQ_ERR_NONFINITE"}
 
 # Every symbol include/mxq.h declares.
-EXPORTS = ("mxq_quantize", "mxq_quantize_noalloc", "mxq_gemm", "mxq_gemm_mixed", "mxq_conv3x3_gemm_mixed",
+EXPORTS = ("mxq_quantize", "mxq_quantize_noalloc", "mxq_quantize_lrp", "mxq_pack_l1t", "mxq_gemm", "mxq_gemm_mixed", "mxq_conv3x3_gemm_mixed",
            "mxq_select_format", "mxq_quantize_mse", "mxq_lowrank_split",
            "mxq_act_format_for_step", "mxq_workspace_size", "mxq_storage",
            "mxq_status_string", "mxq_version")
@@ -66,6 +66,10 @@ def load():
     qp = C.POINTER(QTensorC)
     lib.mxq_quantize.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i32, vp, i64, qp, vp, sz, vp]
     lib.mxq_quantize.restype = i32
+    lib.mxq_quantize_lrp.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i32, vp, i64, qp, vp, sz, vp]
+    lib.mxq_quantize_lrp.restype = i32
+    lib.mxq_pack_l1t.argtypes = [vp, i32, i64, vp, vp]
+    lib.mxq_pack_l1t.restype = i32
     lib.mxq_quantize_noalloc.argtypes = [vp, i32, i64, i64, i64, i32, vp, vp, i32, vp, i64, qp, vp]
     lib.mxq_quantize_noalloc.restype = i32
     lib.mxq_gemm.argtypes = [qp, qp, vp, vp, i64, vp, i32, vp, vp, i64, i64, vp, sz, vp]
@@ -173,9 +177,22 @@ def bf16_operand(x) -> QTensor:
     return QTensor(BF16, x.shape[0], x.shape[1], x, None)
 
 
+def pack_l1t(l1t, stream=None):
+    """mxq_pack_l1t: L1^T [rank, cols] bf16 (cuda) into the packed order the
+    fused quantize + low-rank kernel reads; returned with the same shape."""
+    import torch
+    lib = load()
+    rank, cols = l1t.shape
+    l1t = l1t.contiguous()
+    out = torch.empty_like(l1t)
+    _check("mxq_pack_l1t", lib.mxq_pack_l1t(_ptr(l1t), rank, cols, _ptr(out), _stream(stream)))
+    return out
+
+
 def quantize(x, fmt: int, hadamard: int = 0, static_tensor_scale=None, l1t=None, u=None,
-             out: QTensor | None = None, workspace=None, stream=None) -> QTensor:
-    """mxq_quantize on a 2-D torch tensor (float32 or bfloat16, cuda)."""
+             out: QTensor | None = None, workspace=None, stream=None, l1p=None) -> QTensor:
+    """mxq_quantize on a 2-D torch tensor (float32 or bfloat16, cuda); with
+    ``l1p`` (L1 from pack_l1t) instead of ``l1t``, mxq_quantize_lrp."""
     import torch
     lib = load()
     rows, cols = x.shape
@@ -186,6 +203,13 @@ def quantize(x, fmt: int, hadamard: int = 0, static_tensor_scale=None, l1t=None,
         n = workspace_size(OP_QUANTIZE, rows, cols, fmt)
         workspace = torch.empty((max(n, 16),), dtype=torch.uint8, device=x.device)
     qc = out.c()
+    if l1p is not None:
+        st = lib.mxq_quantize_lrp(_ptr(x), dt, rows, cols, x.stride(0), hadamard,
+                                  _ptr(static_tensor_scale), _ptr(l1p), l1p.shape[0], _ptr(u),
+                                  0 if u is None else u.stride(0), C.byref(qc), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+        _check("mxq_quantize_lrp", st)
+        return out
     rank = 0 if l1t is None else l1t.shape[0]
     st = lib.mxq_quantize(_ptr(x), dt, rows, cols, x.stride(0), hadamard,
                           _ptr(static_tensor_scale), _ptr(l1t), rank, _ptr(u),

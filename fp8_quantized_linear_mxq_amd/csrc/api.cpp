@@ -175,7 +175,8 @@ static mxq_status quantize_impl(const void* x, int32_t dtype, int64_t rows, int6
                                 int64_t ldx, int32_t hadamard_n,
                                 const float* static_tensor_scale, const void* lr_l1t,
                                 int32_t lr_rank, float* lr_u, int64_t ld_u, mxq_qtensor* out,
-                                void* workspace, size_t ws_bytes, bool noalloc, void* stream) {
+                                void* workspace, size_t ws_bytes, bool noalloc, bool packed,
+                                void* stream) {
   if (!out || (dtype != MXQ_DT_F32 && dtype != MXQ_DT_BF16) || rows < 0 || cols < 0)
     return MXQ_ERR_INVALID_ARG;
   if (!known_fmt(out->fmt) || out->rows != rows || out->cols != cols) return MXQ_ERR_INVALID_ARG;
@@ -190,6 +191,11 @@ static mxq_status quantize_impl(const void* x, int32_t dtype, int64_t rows, int6
   if (!aligned(x, 16) || (ldx * esz) % 16) return MXQ_ERR_ALIGNMENT;
   mxq_status st = check_qtensor(out);
   if (st != MXQ_OK) return st;
+  if (packed && lr_rank == 0) return MXQ_ERR_INVALID_ARG;
+  // the packed L1 order is read by the fused quantize + projection kernel:
+  // bf16 input, no rotation, columns a multiple of 128
+  if (packed && (dtype != MXQ_DT_BF16 || hadamard_n != 0)) return MXQ_ERR_UNSUPPORTED;
+  if (packed && cols % 128) return MXQ_ERR_SHAPE;
   if (lr_rank > 0) {
     if (dtype != MXQ_DT_BF16) return MXQ_ERR_UNSUPPORTED;
     if (!lr_l1t || !lr_u || ld_u < lr_rank) return MXQ_ERR_INVALID_ARG;
@@ -238,6 +244,7 @@ static mxq_status quantize_impl(const void* x, int32_t dtype, int64_t rows, int6
     l.rank = lr_rank;
     l.u = lr_u;
     l.ld_u = ld_u;
+    l.packed = packed;
     a.lr = &l;
   }
   hipError_t e = launch_quantize(a, as_stream(stream));
@@ -251,7 +258,28 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
                         const void* lr_l1t, int32_t lr_rank, float* lr_u, int64_t ld_u,
                         mxq_qtensor* out, void* workspace, size_t ws_bytes, void* stream) {
   return quantize_impl(x, dtype, rows, cols, ldx, hadamard_n, static_tensor_scale, lr_l1t,
-                       lr_rank, lr_u, ld_u, out, workspace, ws_bytes, false, stream);
+                       lr_rank, lr_u, ld_u, out, workspace, ws_bytes, false, false, stream);
+}
+
+mxq_status mxq_quantize_lrp(const void* x, int32_t dtype, int64_t rows, int64_t cols, int64_t ldx,
+                            int32_t hadamard_n, const float* static_tensor_scale,
+                            const void* lr_l1p, int32_t lr_rank, float* lr_u, int64_t ld_u,
+                            mxq_qtensor* out, void* workspace, size_t ws_bytes, void* stream) {
+  return quantize_impl(x, dtype, rows, cols, ldx, hadamard_n, static_tensor_scale, lr_l1p,
+                       lr_rank, lr_u, ld_u, out, workspace, ws_bytes, false, true, stream);
+}
+
+mxq_status mxq_pack_l1t(const void* l1t, int32_t rank, int64_t cols, void* l1p, void* stream) {
+  if (rank < 16 || rank > 128 || rank % 16 || cols < 0) return MXQ_ERR_INVALID_ARG;
+  if (cols % 128) return MXQ_ERR_SHAPE;
+  if (cols == 0) return MXQ_OK;
+  if (!l1t || !l1p) return MXQ_ERR_INVALID_ARG;
+  if (!aligned(l1t, 16) || !aligned(l1p, 16)) return MXQ_ERR_ALIGNMENT;
+  unsigned* dbg = nullptr;
+  const mxq_status st = device_entry(&dbg);
+  if (st != MXQ_OK) return st;
+  return from_hip(launch_pack_l1t(static_cast<const uint16_t*>(l1t), rank, cols,
+                                  static_cast<uint16_t*>(l1p), as_stream(stream)));
 }
 
 mxq_status mxq_quantize_noalloc(const void* x, int32_t dtype, int64_t rows, int64_t cols,
@@ -260,7 +288,7 @@ mxq_status mxq_quantize_noalloc(const void* x, int32_t dtype, int64_t rows, int6
                                 int32_t lr_rank, float* lr_u, int64_t ld_u, mxq_qtensor* out,
                                 void* stream) {
   return quantize_impl(x, dtype, rows, cols, ldx, hadamard_n, static_tensor_scale, lr_l1t,
-                       lr_rank, lr_u, ld_u, out, nullptr, 0, true, stream);
+                       lr_rank, lr_u, ld_u, out, nullptr, 0, true, false, stream);
 }
 
 static mxq_status gemm_checks(const mxq_qtensor* a, const mxq_qtensor* w, const float* lr_u,

@@ -9,12 +9,20 @@ namespace mxq {
 struct LoraDownArgs {
   const uint16_t* x;   // bf16 [rows][ldx]
   int64_t rows, cols, ldx;
-  const uint16_t* l1t; // bf16 [rank][cols]
+  const uint16_t* l1t; // bf16 [rank][cols], or the packed order below
   int rank;
   float* u;            // [rows][ld_u]
   int64_t ld_u;
+  bool packed;         // l1t in the fragment order of launch_pack_l1t
 };
 hipError_t launch_lora_down(const LoraDownArgs& a, hipStream_t s);
+
+// L1^T [rank][cols] (bf16, row stride cols) into the order the fused
+// quantize + low-rank kernel reads: 16-byte piece i = ((g NT + t) 4 + j) 64
+// + lane holds L1^T[16t + lane % 16][128g + 32(lane / 16) + 8j + [0, 8)],
+// NT = rank / 16 (rank a multiple of 16, cols a multiple of 128).
+hipError_t launch_pack_l1t(const uint16_t* l1t, int rank, int64_t cols, uint16_t* l1p,
+                           hipStream_t s);
 
 struct QuantizeArgs {
   const void* x;

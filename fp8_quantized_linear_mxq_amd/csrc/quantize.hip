@@ -501,7 +501,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_onepass_kernel(QParams p, uint
 constexpr int kLrRows = 16;
 constexpr int kLrWaves = 8;
 
-template <int FMT, int NT>
+template <int FMT, int NT, bool PK>
 __global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, LoraDownArgs lr) {
   constexpr int U = NT <= 2 ? 2 : 1;   // groups in flight per wave
   __shared__ float part[kLrWaves][kLrRows][16 * NT];
@@ -512,7 +512,11 @@ __global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, L
   const bool row_ok = m0 + r16 < lr.rows;
   const int64_t row = row_ok ? m0 + r16 : lr.rows - 1;
   const uint16_t* xr = lr.x + row * lr.ldx + kq * 32;
-  const uint16_t* lp = lr.l1t + (int64_t)r16 * lr.cols + kq * 32;
+  // L1^T fragments: [rank][cols] rows (a lane's 16 bytes of one rank row,
+  // 64 bytes apart across the lane's K-quarter: 32 cache lines per wave load)
+  // or the packed order (one contiguous kilobyte per wave load; the
+  // fragment reads of the kernel cost about a quarter less time).
+  const uint16_t* lp = PK ? lr.l1t + lane * 8 : lr.l1t + (int64_t)r16 * lr.cols + kq * 32;
   const int groups = (int)(lr.cols / 128);
   v4f acc[NT];
 #pragma unroll
@@ -528,7 +532,9 @@ __global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, L
         xv[u][j] = ok ? *reinterpret_cast<const uint4*>(xr + gi * 128 + 8 * j) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          lv[u][t][j] = ok ? *reinterpret_cast<const uint4*>(lp + (int64_t)t * 16 * lr.cols + gi * 128 + 8 * j)
+          lv[u][t][j] = ok ? *reinterpret_cast<const uint4*>(
+                                 PK ? lp + (((int64_t)gi * NT + t) * 4 + j) * 512
+                                    : lp + (int64_t)t * 16 * lr.cols + gi * 128 + 8 * j)
                            : make_uint4(0, 0, 0, 0);
       }
     }
@@ -621,20 +627,39 @@ __global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, L
   }
 }
 
-template <int FMT>
-hipError_t launch_lr(int nt, dim3 grid, const QParams& p, const LoraDownArgs& lr, hipStream_t s) {
+template <int FMT, bool PK>
+hipError_t launch_lr_pk(int nt, dim3 grid, const QParams& p, const LoraDownArgs& lr, hipStream_t s) {
   switch (nt) {
-    case 1: quantize_lr_kernel<FMT, 1><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
-    case 2: quantize_lr_kernel<FMT, 2><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
-    case 3: quantize_lr_kernel<FMT, 3><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
-    case 4: quantize_lr_kernel<FMT, 4><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
-    case 5: quantize_lr_kernel<FMT, 5><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
-    case 6: quantize_lr_kernel<FMT, 6><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
-    case 7: quantize_lr_kernel<FMT, 7><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
-    case 8: quantize_lr_kernel<FMT, 8><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 1: quantize_lr_kernel<FMT, 1, PK><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 2: quantize_lr_kernel<FMT, 2, PK><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 3: quantize_lr_kernel<FMT, 3, PK><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 4: quantize_lr_kernel<FMT, 4, PK><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 5: quantize_lr_kernel<FMT, 5, PK><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 6: quantize_lr_kernel<FMT, 6, PK><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 7: quantize_lr_kernel<FMT, 7, PK><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
+    case 8: quantize_lr_kernel<FMT, 8, PK><<<grid, 64 * kLrWaves, 0, s>>>(p, lr); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_lr(int nt, dim3 grid, const QParams& p, const LoraDownArgs& lr, hipStream_t s) {
+  return lr.packed ? launch_lr_pk<FMT, true>(nt, grid, p, lr, s)
+                   : launch_lr_pk<FMT, false>(nt, grid, p, lr, s);
+}
+
+// One thread per 16-byte piece of the packed order (see launch_pack_l1t).
+__global__ __launch_bounds__(256) void pack_l1t_kernel(const uint16_t* l1t, int nt, int64_t cols,
+                                                       uint16_t* l1p, int64_t pieces) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  const int lane = (int)(i & 63), j = (int)((i >> 6) & 3);
+  const int64_t rest = i >> 8;
+  const int t = (int)(rest % nt);
+  const int64_t g = rest / nt;
+  const uint16_t* src = l1t + (int64_t)(t * 16 + (lane & 15)) * cols + g * 128 + (lane >> 4) * 32 + 8 * j;
+  *reinterpret_cast<uint4*>(l1p + i * 8) = *reinterpret_cast<const uint4*>(src);
 }
 
 // ---------------------------------------------------------------------------
@@ -911,6 +936,15 @@ hipError_t nonfinite_flag_ptr(unsigned** out) {
   return hipSuccess;
 }
 
+hipError_t launch_pack_l1t(const uint16_t* l1t, int rank, int64_t cols, uint16_t* l1p,
+                           hipStream_t s) {
+  const int64_t pieces = (int64_t)rank * cols / 8;
+  if (pieces == 0) return hipSuccess;
+  pack_l1t_kernel<<<dim3((unsigned)((pieces + 255) / 256)), 256, 0, s>>>(l1t, rank / 16, cols, l1p,
+                                                                        pieces);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
   QParams p;
   p.x = a.x;
@@ -961,6 +995,9 @@ hipError_t launch_quantize(const QuantizeArgs& a, hipStream_t s) {
         default: return hipErrorInvalidValue;
       }
     }
+    // the packed order is read by the fused kernel only (its conditions are
+    // checked before any launch)
+    if (a.lr->packed) return hipErrorInvalidValue;
     // rotated activations (or columns not a multiple of 128): quantize, then
     // u from the unrotated x in its own pass
     hipError_t e = (a.dtype == DT_BF16)

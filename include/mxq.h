@@ -173,6 +173,36 @@ mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols
                         void* stream);
 
 /*
+ * mxq_pack_l1t -- rearrange the first low-rank factor L1^T [rank][cols]
+ * (bf16, row stride cols, K contiguous) into the order in which the fused
+ * quantize + low-rank kernel reads it (Nunchaku article, main explanation:
+ * L1 is part of the weight, prepared once).  Same size, rank * cols bf16:
+ * 16-byte piece i = ((g * rank/16 + t) * 4 + j) * 64 + l holds
+ * L1^T[16 t + l % 16][128 g + 32 (l / 16) + 8 j + (0 .. 7)], so one wave's
+ * load of a fragment set is one contiguous kilobyte.  l1t and l1p are device
+ * pointers, 16-byte aligned, not overlapping; rank a multiple of 16 in
+ * [16, 128]; cols a multiple of 128 (else MXQ_ERR_SHAPE).  Enqueued on stream.
+ */
+mxq_status mxq_pack_l1t(const void* l1t, int32_t rank, int64_t cols, void* l1p, void* stream);
+
+/*
+ * mxq_quantize_lrp -- mxq_quantize with the low-rank factor given in the
+ * packed order of mxq_pack_l1t (lr_l1p) instead of L1^T rows.  Same results
+ * (codes, scales, tensor scale and u bit-identical to mxq_quantize with the
+ * unpacked L1^T); the projection's factor reads are whole contiguous
+ * kilobytes.  It takes the fused quantize + projection path only: lr_rank a
+ * multiple of 16 in [16, 128] (0 is MXQ_ERR_INVALID_ARG), bf16 x and
+ * hadamard_n 0 (else MXQ_ERR_UNSUPPORTED), cols a multiple of 128 (else
+ * MXQ_ERR_SHAPE).  Other arguments, workspace and errors as mxq_quantize.
+ */
+mxq_status mxq_quantize_lrp(const void* x, int32_t dtype, int64_t rows, int64_t cols,
+                            int64_t ldx, int32_t hadamard_n,
+                            const float* static_tensor_scale,
+                            const void* lr_l1p, int32_t lr_rank, float* lr_u, int64_t ld_u,
+                            mxq_qtensor* out, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/*
  * mxq_quantize_noalloc -- mxq_quantize with no workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  Same arguments,

@@ -131,6 +131,31 @@ def test_validation_before_device_work(lib):
                                  None, 0, None) == 4
 
 
+def test_validation_of_packed_lowrank_entry_points(lib):
+    """mxq_pack_l1t and mxq_quantize_lrp reject bad arguments before any
+    device work (no GPU here): rank, shape, alignment, and the conditions of
+    the fused path (bf16 x, no rotation, columns a multiple of 128)."""
+    vp = C.c_void_p
+    pack = lib.mxq_pack_l1t
+    assert pack(vp(4096), 8, 256, vp(8192), None) == 1        # rank not a multiple of 16
+    assert pack(vp(4096), 144, 256, vp(8192), None) == 1      # rank above 128
+    assert pack(vp(4096), 32, 192, vp(8192), None) == 4       # cols not a multiple of 128
+    assert pack(vp(4096), 32, 0, vp(8192), None) == 0         # empty: no-op
+    assert pack(None, 32, 256, vp(8192), None) == 1
+    assert pack(vp(4100), 32, 256, vp(8192), None) == 3       # misaligned
+    lrp = lib.mxq_quantize_lrp
+    q = _lib.QTensorC(1, 0, 4, 256, vp(4096), 128, vp(8192), 8, None)
+    u = vp(65536)
+    # rank 0, f32 input, rotation, cols not a multiple of 128
+    assert lrp(vp(16), 2, 4, 256, 256, 0, None, vp(32768), 0, u, 32, C.byref(q), None, 0, None) == 1
+    assert lrp(vp(16), 1, 4, 256, 256, 0, None, vp(32768), 32, u, 32, C.byref(q), None, 0, None) == 2
+    assert lrp(vp(16), 2, 4, 256, 256, 16, None, vp(32768), 32, u, 32, C.byref(q), None, 0, None) == 2
+    q160 = _lib.QTensorC(1, 0, 4, 160, vp(4096), 80, vp(8192), 8, None)
+    assert lrp(vp(16), 2, 4, 160, 160, 0, None, vp(32768), 32, u, 32, C.byref(q160), None, 0, None) == 4
+    # missing u
+    assert lrp(vp(16), 2, 4, 256, 256, 0, None, vp(32768), 32, None, 32, C.byref(q), None, 0, None) == 1
+
+
 def test_status_codes_and_no_device(lib):
     assert lib.mxq_status_string(8).startswith(b"NaN or Inf")
     assert _lib.STATUS[8] == "MXQ_ERR_NONFINITE"

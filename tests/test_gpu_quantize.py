@@ -171,3 +171,63 @@ def test_nvfp4_thresholds_just_above_a_midpoint():
         q = mxq.quantize(xd, mxq.NVFP4, static_tensor_scale=gd)
         assert np.array_equal(gu.dev_scales(q, "NVFP4"), want["scales"])
         assert np.array_equal(gu.unpack_dev_codes(q, "NVFP4"), want["codes"]), dtype
+
+
+def _packed_l1t(l1t: np.ndarray) -> np.ndarray:
+    """The packed order of mxq_pack_l1t written out: 16-byte piece
+    i = ((g * rank/16 + t) * 4 + j) * 64 + l holds
+    L1^T[16 t + l % 16][128 g + 32 (l // 16) + 8 j + (0..7)]."""
+    rank, cols = l1t.shape
+    nt, pieces = rank // 16, rank * cols // 8
+    i = np.arange(pieces)
+    lane, j, rest = i & 63, (i >> 6) & 3, i >> 8
+    t, g = rest % nt, rest // nt
+    row = t * 16 + lane % 16
+    col0 = g * 128 + (lane // 16) * 32 + 8 * j
+    return l1t[row[:, None], col0[:, None] + np.arange(8)].reshape(rank, cols)
+
+
+@pytest.mark.parametrize("rank,cols", [(16, 128), (32, 640), (48, 1152), (128, 256), (32, 3072)])
+def test_pack_l1t_layout(rank, cols):
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    rng = np.random.default_rng(rank + cols)
+    bits = rng.integers(0, 1 << 16, size=(rank, cols), dtype=np.uint16)
+    gu.say(f"pack L1^T rank {rank} cols {cols}")
+    got = mxq.pack_l1t(gu.to_dev_bf16(bits))
+    torch.cuda.synchronize()
+    got = got.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, _packed_l1t(bits))
+
+
+@pytest.mark.parametrize("fmt,r,m,k", [("MXFP4", 32, 4096, 3072), ("MXFP4", 16, 100, 640),
+                                        ("MXFP8", 32, 37, 256), ("NVFP4", 48, 100, 1152),
+                                        ("INT4", 128, 21, 384), ("NVFP4", 32, 300, 1024)])
+def test_quantize_with_packed_l1(fmt, r, m, k):
+    """mxq_quantize_lrp (L1 in the packed order) equals mxq_quantize (L1^T
+    rows) bit for bit: codes, scales, tensor scale and u; ragged rows and the
+    SVDQuant layer's 4096 x 3072 activation."""
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    rng = np.random.default_rng(3 * r + m + k)
+    xb = wl.f32_to_bf16_bits((rng.standard_t(3, size=(m, k)) * 3).astype(np.float32))
+    l1 = wl.f32_to_bf16_bits(rng.normal(0, 0.02, size=(r, k)).astype(np.float32))
+    xd, l1d = gu.to_dev_bf16(xb), gu.to_dev_bf16(l1)
+    gu.say(f"quantize {fmt} with packed L1, rank {r}, {m}x{k}")
+    ua = torch.empty((m, r), dtype=torch.float32, device="cuda")
+    ub = torch.empty((m, r), dtype=torch.float32, device="cuda")
+    qa = mxq.quantize(xd, gu.FMT_ID[fmt], l1t=l1d, u=ua)
+    qb = mxq.quantize(xd, gu.FMT_ID[fmt], l1p=mxq.pack_l1t(l1d), u=ub)
+    torch.cuda.synchronize()
+    assert torch.equal(ua, ub)
+    assert np.array_equal(gu.dev_scales(qa, fmt), gu.dev_scales(qb, fmt))
+    assert np.array_equal(gu.unpack_dev_codes(qa, fmt), gu.unpack_dev_codes(qb, fmt))
+    if fmt == "NVFP4":
+        assert torch.equal(qa.tensor_scale, qb.tensor_scale)
+    if m <= 512:
+        want = gu.oracle_quant(wl.bf16_to_f32(xb), fmt, mant_bits=7)
+        assert np.array_equal(gu.unpack_dev_codes(qb, fmt), want["codes"])
+        x64 = wl.bf16_to_f32(xb).astype(np.float64)
+        lv = wl.bf16_to_f32(l1).astype(np.float64).T
+        err = np.abs(ub.cpu().numpy().astype(np.float64) - x64 @ lv)
+        assert np.all(err <= 1e-5 * (np.abs(x64) @ np.abs(lv)))
