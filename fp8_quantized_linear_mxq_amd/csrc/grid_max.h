@@ -68,7 +68,7 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Called by all 64 lanes of wave 0 with the workgroup's maximum m (the same
 // value in every lane); returns the grid's maximum (NaN on a timeout).
-__device__ __noinline__ float grid_max_wave0(GridMaxSlot* s, float m) {
+__device__ __forceinline__ float grid_max_wave0(GridMaxSlot* s, float m) {
   const int lane = threadIdx.x & 63;
   const unsigned nwg = gridDim.x, b = blockIdx.x, k = b / kGroup;
   const unsigned ngroups = (nwg + kGroup - 1) / kGroup;
