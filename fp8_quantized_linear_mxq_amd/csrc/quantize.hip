@@ -422,14 +422,15 @@ __global__ __launch_bounds__(kThreads) void amax32_kernel(QParams p, float* part
 // this device (the two-pass kernels take inputs that do not fit).  A call
 // whose grid could not become resident within about a second (other work
 // holding the compute units) writes a NaN tensor scale.  Consecutive calls
-// take different barrier slots of a small ring; calls ordered on one stream
-// reuse them safely.
+// take different barrier slots of a small ring (a static array per device,
+// zero at load; kernels get its device address, looked up once per device);
+// calls ordered on one stream reuse them safely.
 constexpr int kNvSlots = 16;
-__device__ GridMaxSlot g_nvslot[kNvSlots];
+static __device__ __align__(256) GridMaxSlot g_nvslot[kNvSlots];
 
 template <int DT, int HAD, int J>
 __global__ __launch_bounds__(kThreads) void nvfp4_onepass_kernel(QParams p, uint32_t bpr,
-                                                                 uint32_t nblk, int slot) {
+                                                                 uint32_t nblk, GridMaxSlot* slot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t b0 = blockIdx.x * (kThreads * J) + threadIdx.x;
   float v[J][4][8];
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_onepass_kernel(QParams p, uint
     float wm = red[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) wm = fmaxf(wm, red[w]);
-    const float A = grid_max_wave0(&g_nvslot[slot], wm);
+    const float A = grid_max_wave0(slot, wm);
     // g = RN_fp32(A / 2688): the float64 quotient of two float32 values
     // rounds correctly to float32 (a NaN from a timed-out wait passes on)
     const float g = (float)((double)A / 2688.0);
@@ -858,14 +859,34 @@ int onepass_capacity() {
 
 std::atomic<unsigned> g_next_nvslot{0};
 
+// Device address of the current device's barrier-slot ring (its own copy
+// of g_nvslot), looked up with that device current, once per device.
+GridMaxSlot* nvslot_ring() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<GridMaxSlot*> cache[kMaxDev];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+  GridMaxSlot* ptr = cache[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(g_nvslot)) != hipSuccess || !a) return nullptr;
+    ptr = static_cast<GridMaxSlot*>(a);
+    cache[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
 // The one-pass kernel with J blocks per lane, if its grid is resident at
 // once on this device; false leaves the work to the two-pass kernels.
 template <int DT, int HAD, int J>
 bool onepass_j(const QParams& p, uint32_t bpr, uint32_t nblk, hipStream_t s, hipError_t* err) {
   const uint64_t grid = ((uint64_t)nblk + kThreads * J - 1) / (kThreads * J);
   if (grid > (uint64_t)onepass_capacity<DT, HAD, J>() || grid > (uint64_t)kGridMaxWgs) return false;
+  GridMaxSlot* ring = nvslot_ring();
+  if (!ring) return false;
   const int slot = (int)(g_next_nvslot.fetch_add(1u, std::memory_order_relaxed) % kNvSlots);
-  nvfp4_onepass_kernel<DT, HAD, J><<<dim3((unsigned)grid), kThreads, 0, s>>>(p, bpr, nblk, slot);
+  nvfp4_onepass_kernel<DT, HAD, J><<<dim3((unsigned)grid), kThreads, 0, s>>>(p, bpr, nblk,
+                                                                             ring + slot);
   *err = hipGetLastError();
   return true;
 }

@@ -206,13 +206,14 @@ mxq_status mxq_quantize_lrp(const void* x, int32_t dtype, int64_t rows, int64_t 
  * mxq_quantize_noalloc -- mxq_quantize with no workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  Same arguments,
- * results and errors as mxq_quantize; the scratch the dynamic NVFP4 tensor
- * scale needs (its amax partials, at most 1024 floats whatever the input
- * size, so no input is too large for it) lives in a 4 KB array of the
- * library's own, one per device, held until the process ends.  The library
- * looks up that array's address on the first call on each device (that call
- * must run with the device current); nothing is allocated or freed, here or
- * later.  Calls on one device share the array: calls that overlap in time on
+ * results and errors as mxq_quantize.  The dynamic NVFP4 tensor scale in
+ * its one-pass form uses the library's barrier slots, as mxq_quantize does;
+ * in its two-pass form the scratch it needs (its amax partials, at most 1024
+ * floats whatever the input size, so no input is too large for it) lives in
+ * a 4 KB array of the library's own, one per device, held until the process
+ * ends.  The library looks up the address of each such array on the first
+ * call on each device (that call must run with the device current); nothing
+ * is allocated or freed, here or later.  Calls on one device share the array: calls that overlap in time on
  * one device (different streams, no ordering between them) race and may
  * produce wrong NVFP4 tensor scales; calls ordered on one stream do not.
  */

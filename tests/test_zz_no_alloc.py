@@ -27,9 +27,16 @@ def _noalloc(lib, x, fmt, had, out, stream):
     assert st == 0, _lib.STATUS.get(st, st)
 
 
+@pytest.mark.parametrize("two_pass", [False, True])
 @pytest.mark.parametrize("fmt,had,dtype", CASES)
-def test_noalloc_matches_quantize(lib, fmt, had, dtype):
+def test_noalloc_matches_quantize(lib, fmt, had, dtype, two_pass, monkeypatch):
+    """Dynamic NVFP4 takes the one-pass kernel (barrier slots) by default; with
+    MXQ_NVFP4_TWO_PASS=1 its amax partials go through the scratch array."""
     import torch
+    if two_pass:
+        if fmt != "NVFP4":
+            pytest.skip("the two passes concern the dynamic NVFP4 scale only")
+        monkeypatch.setenv("MXQ_NVFP4_TWO_PASS", "1")
 
     import fp8_quantized_linear_mxq_amd as mxq
     stream = torch.cuda.current_stream()
