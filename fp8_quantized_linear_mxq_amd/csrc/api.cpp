@@ -183,7 +183,8 @@ static mxq_status quantize_impl(const void* x, int32_t dtype, int64_t rows, int6
   if (hadamard_n != 0 && hadamard_n != 16 && hadamard_n != 32 && hadamard_n != 128)
     return MXQ_ERR_INVALID_ARG;
   if (lr_rank < 0 || lr_rank > 128 || lr_rank % 16) return MXQ_ERR_INVALID_ARG;
-  if (cols % block_of(out->fmt) || (hadamard_n && cols % hadamard_n)) return MXQ_ERR_SHAPE;
+  // the kernels take 32-element runs of a row (NVFP4's 16-blocks in pairs)
+  if (cols % 32 || (hadamard_n && cols % hadamard_n)) return MXQ_ERR_SHAPE;
   if (rows == 0 || cols == 0) return MXQ_OK;
   if (rows * (cols / 8) >= (int64_t)1 << 32) return MXQ_ERR_SHAPE;
   if (!x || ldx < cols) return MXQ_ERR_INVALID_ARG;

@@ -162,8 +162,9 @@ typedef struct mxq_qtensor {
  *              tensor scale used is written to *out->tensor_scale.
  *  workspace   device scratch of mxq_workspace_size(MXQ_OP_QUANTIZE, ...)
  *              bytes (only dynamic NVFP4 needs any).
- * Returns MXQ_ERR_SHAPE when cols is not a multiple of the block (32, or 16
- * for NVFP4) or of hadamard_n.  rows == 0 is a no-op.
+ * Returns MXQ_ERR_SHAPE when cols is not a multiple of 32 (for NVFP4 too:
+ * its 16-blocks are quantized in pairs) or of hadamard_n.  rows == 0 is a
+ * no-op.
  */
 mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols,
                         int64_t ldx, int32_t hadamard_n,

@@ -79,6 +79,10 @@ def test_validation_before_device_work(lib):
     assert lib.mxq_quantize(vp(16), 1, 4, 64, 64, 0, None, None, 8, None, 0, C.byref(q), None, 0, None) == 1
     q48 = _lib.QTensorC(1, 0, 4, 48, None, 32, None, 2, None)
     assert lib.mxq_quantize(vp(16), 1, 4, 48, 48, 0, None, None, 0, None, 0, C.byref(q48), None, 0, None) == 4
+    # NVFP4 too: 16-blocks are quantized in pairs, so K must be a multiple of 32
+    qn48 = _lib.QTensorC(3, 0, 4, 48, vp(4096), 32, vp(8192), 4, vp(12288))
+    assert lib.mxq_quantize(vp(16), 1, 4, 48, 48, 0, None, None, 0, None, 0, C.byref(qn48), vp(65536),
+                            4096, None) == 4
     # misaligned input pointer
     qo = _lib.QTensorC(1, 0, 4, 64, vp(4096), 32, vp(8192), 4, None)
     assert lib.mxq_quantize(vp(18), 1, 4, 64, 64, 0, None, None, 0, None, 0, C.byref(qo), None, 0, None) == 3
