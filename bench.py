@@ -408,17 +408,56 @@ def main() -> int:
         else:
             mxq.gemm(s["qa"], s["qw"], u=s["u"], l2t=s["l2t"], out=s["out"], workspace=s["ws"])
 
-    def step(s, i):
-        quant(s, i)
+    def route(s, i):
+        # the activation format of step i from the timestep table (host)
+        if mixed and not bf16_act:
+            f = mxq.act_format_for_step(act_table, 1, wl.ACT_TABLE_BUCKETS, 0, i % num_steps,
+                                        num_steps)
+            if f != s["qa"].fmt:
+                raise RuntimeError(f"table routes format {f}; the buffers hold {s['qa'].fmt}")
+
+    # A step is the layer's launches (quantize, then GEMM) on one buffer set.
+    # The steps are replayed from HIP graphs: one graph holds a whole round
+    # of steps over every buffer set in order, so neither a small layer's
+    # launches nor a graph launch per step sets the pace; a count of steps
+    # that is not a whole number of rounds ends with one-step graphs.  The
+    # routing lookup still runs on the host for every step.  Graph replays
+    # are bit-identical to the eager calls (tests/test_gpu_graph.py).
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            fn()
+        return g
+
+    def one(s):
+        quant(s)
         gemm(s)
 
-    for i in range(args.warmup):
-        step(sets[i % n_sets], i)
+    round_graph = capture(lambda: [one(s) for s in sets])
+    step_graphs = [capture(lambda s=s: one(s)) for s in sets]
+    torch.cuda.synchronize()
+
+    def run_steps(first, count):
+        i = first
+        while i < first + count:
+            if i % n_sets == 0 and first + count - i >= n_sets:
+                for k in range(n_sets):
+                    route(sets[k], i + k)
+                round_graph.replay()
+                i += n_sets
+            else:
+                route(sets[i % n_sets], i)
+                step_graphs[i % n_sets].replay()
+                i += 1
+
+    run_steps(0, args.warmup)
     torch.cuda.synchronize()
     # timed region: exactly `steps` steps, wall clock, synchronized both sides
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(sets[i % n_sets], i)
+    run_steps(0, args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     # per-kernel durations: each kernel's launches over all buffer sets are
