@@ -417,10 +417,10 @@ def main() -> int:
                 raise RuntimeError(f"table routes format {f}; the buffers hold {s['qa'].fmt}")
 
     # A step is the layer's launches (quantize, then GEMM) on one buffer set.
-    # The steps are replayed from HIP graphs: one graph holds a whole round
-    # of steps over every buffer set in order, so neither a small layer's
+    # The steps are replayed from HIP graphs: one graph holds a sweep of
+    # steps over every buffer set in order, so neither a small layer's
     # launches nor a graph launch per step sets the pace; a count of steps
-    # that is not a whole number of rounds ends with one-step graphs.  The
+    # that is not a whole number of sweeps ends with one-step graphs.  The
     # routing lookup still runs on the host for every step.  Graph replays
     # are bit-identical to the eager calls (tests/test_gpu_graph.py).
     cap = torch.cuda.Stream()
@@ -436,7 +436,7 @@ def main() -> int:
         quant(s)
         gemm(s)
 
-    round_graph = capture(lambda: [one(s) for s in sets])
+    sweep_graph = capture(lambda: [one(s) for s in sets])
     step_graphs = [capture(lambda s=s: one(s)) for s in sets]
     torch.cuda.synchronize()
 
@@ -446,7 +446,7 @@ def main() -> int:
             if i % n_sets == 0 and first + count - i >= n_sets:
                 for k in range(n_sets):
                     route(sets[k], i + k)
-                round_graph.replay()
+                sweep_graph.replay()
                 i += n_sets
             else:
                 route(sets[i % n_sets], i)
