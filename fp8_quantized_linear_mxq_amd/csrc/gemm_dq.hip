@@ -179,8 +179,10 @@ struct Fp4Loader {
   template <bool FP16>
   __device__ void convert(const Fp4Data& d, uint4 o[4]) const {
     if constexpr (KIND == K_NV) {
-      dq_fp4_nv<FP16>(d.r, e4m3_value((d.s >> (16 * fc)) & 0xFFu),
-                      e4m3_value((d.s >> (16 * fc + 8)) & 0xFFu), o);
+      // the lane's two E4M3 block scales, decoded exactly by the hardware
+      // FP8 convert (a power-of-two scale of 1)
+      const v2f s = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d.s >> (16 * fc), 1.0f, false);
+      dq_fp4_nv<FP16>(d.r, s.x, s.y, o);
     } else if constexpr (KIND == K_MX4) {
       dq_fp4_mx(d.r, e8m0_f32<K_MX4>(d.s), o);
     } else {

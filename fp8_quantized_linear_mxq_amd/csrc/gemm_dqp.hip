@@ -97,9 +97,16 @@ __device__ __forceinline__ Scales<K, FP16> lane_scales(uint32_t dw, int half) {
   if constexpr (K == K_BF) {
     r.s[0] = r.s[1] = 1.0f;   // no scales
   } else if constexpr (K == K_NV) {
-    // dword `half` of the row's 8 scale bytes: 16-blocks 4h .. 4h+3
-#pragma unroll
-    for (int q = 0; q < 4; ++q) r.s[q] = e4m3_value((dw >> (8 * q)) & 0xFFu);
+    // dword `half` of the row's 8 scale bytes: 16-blocks 4h .. 4h+3.  The
+    // hardware FP8 converts decode the four E4M3 codes exactly (a power-of-
+    // two scale of 1), two per instruction, in place of a bit-field decode
+    // of about seven instructions per code.
+    const v2f lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(dw, 1.0f, false);
+    const v2f hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(dw, 1.0f, true);
+    r.s[0] = lo.x;
+    r.s[1] = lo.y;
+    r.s[2] = hi.x;
+    r.s[3] = hi.y;
   } else {
     // bytes 2h, 2h+1 of the row's 4 scale bytes: 32-blocks 2h, 2h+1
     const uint32_t b = dw >> (16 * half);
