@@ -282,3 +282,52 @@ def test_gemm_tiny_block_scales(fa, fw):
     r = gu.check_gemm(y, a_deq, gu.dequant_w_for_gemm(qw), gu.alpha_of(qa, qw),
                       tag=f"{fa}x{fw} tiny")
     gu.say(f"  worst err/tol {r:.3g}")
+
+
+def _every_e4m3_scale(rows, k, seed):
+    """Values whose 16-blocks, quantized to NVFP4 with the static tensor
+    scale g = 1, take every E4M3 block-scale code 0 .. 126 in turn (the
+    subnormal codes 1 .. 7 included): block b's amax is 6 * E4M3(b % 127)."""
+    from oracle import formats as of
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(-1.0, 1.0, size=(rows, k // 16, 16))
+    code = np.arange(rows * (k // 16)).reshape(rows, k // 16) % 127
+    amax = 6.0 * np.vectorize(of.e4m3_value)(code).astype(np.float64)
+    x[:, :, 0] = np.where(rng.random((rows, k // 16)) < 0.5, -1.0, 1.0)   # |max| = 1 exactly
+    return (x * amax[:, :, None]).reshape(rows, k).astype(np.float32), code
+
+
+@pytest.mark.parametrize("fa,fw", [("NVFP4", "NVFP4"), ("MXFP8", "NVFP4"), ("MXFP4", "NVFP4"),
+                                   ("NVFP4", "MXFP4"), ("NVFP4", "INT4")])
+def test_gemm_every_e4m3_block_scale(fa, fw):
+    """The NVFP4 operand's block scales cover every E4M3 code (subnormal
+    ones too), decoded in the GEMM by the hardware FP8 converts: results
+    within the bound on every route that reads NVFP4 scales."""
+    import torch
+    import fp8_quantized_linear_mxq_amd as mxq
+    m, n, k = 48, 40, 512
+    gu.say(f"gemm every E4M3 block scale {fa}x{fw} M={m} N={n} K={k}")
+    rng = np.random.default_rng(31)
+    one = torch.ones(1, dtype=torch.float32, device="cuda")
+    if fa == "NVFP4":
+        a, code = _every_e4m3_scale(m, k, seed=5)
+        qa_dev = mxq.quantize(gu.to_dev_f32(a), mxq.NVFP4, static_tensor_scale=one)
+        qa = oq.quantize(a, "NVFP4", tensor_scale=1.0)
+        assert np.array_equal(qa["scales"], code)            # every code present
+    else:
+        a = (rng.standard_t(3, size=(m, k)) * 2.0).astype(np.float32)
+        qa = oq.quantize(a, fa)
+        qa_dev = gu.qtensor_from_oracle(qa, m, k)
+    if fw == "NVFP4":
+        w, code = _every_e4m3_scale(n, k, seed=6)
+        qw_dev = mxq.quantize(gu.to_dev_f32(w), mxq.NVFP4, static_tensor_scale=one)
+        qw = oq.quantize(w, "NVFP4", tensor_scale=1.0)
+        assert np.array_equal(qw["scales"], code)
+    else:
+        w = rng.normal(0, 0.02, size=(n, k)).astype(np.float32)
+        qw = oq.quantize(w, fw)
+        qw_dev = gu.qtensor_from_oracle(qw, n, k)
+    y = mxq.gemm(qa_dev, qw_dev)
+    r = gu.check_gemm(y, gu.dequant_a_for_gemm(qa), gu.dequant_w_for_gemm(qw), gu.alpha_of(qa, qw),
+                      tag=f"{fa}x{fw} every E4M3 scale")
+    gu.say(f"  worst err/tol {r:.3g}")
