@@ -10,21 +10,23 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-CASES = [  # (activation format, weight format, hadamard, rank)
-    ("MXFP8", "MXFP4", 0, 0),
-    ("NVFP4", "NVFP4", 16, 0),
-    ("MXFP4", "MXFP4", 0, 32),
-    ("MXFP8", "NVFP4", 0, 16),
+CASES = [  # (activation format, weight format, hadamard, rank, L1 packed)
+    ("MXFP8", "MXFP4", 0, 0, False),
+    ("NVFP4", "NVFP4", 16, 0, False),
+    ("MXFP4", "MXFP4", 0, 32, False),
+    ("MXFP4", "MXFP4", 0, 32, True),
+    ("MXFP8", "NVFP4", 0, 16, False),
+    ("NVFP4", "MXFP4", 0, 16, True),
 ]
 
 
-@pytest.mark.parametrize("fa,fw,had,rank", CASES)
-def test_graph_replay_matches_eager(fa, fw, had, rank):
+@pytest.mark.parametrize("fa,fw,had,rank,packed", CASES)
+def test_graph_replay_matches_eager(fa, fw, had, rank, packed):
     import torch
     import fp8_quantized_linear_mxq_amd as mxq
     m, k, n = 300, 1024, 520
-    gu.say(f"graph replay {fa}x{fw} had={had} rank={rank}")
-    rng = np.random.default_rng(11 + rank + had)
+    gu.say(f"graph replay {fa}x{fw} had={had} rank={rank} packed={packed}")
+    rng = np.random.default_rng(11 + rank + had + packed)
     x = gu.to_dev_bf16(wl.f32_to_bf16_bits((rng.standard_t(3, size=(m, k)) * 2).astype(np.float32)))
     wf = gu.to_dev_f32(rng.normal(0, 0.02, size=(n, k)).astype(np.float32))
     qw = mxq.quantize(wf, gu.FMT_ID[fw], hadamard=had)
@@ -41,8 +43,13 @@ def test_graph_replay_matches_eager(fa, fw, had, rank):
         y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
         return q, u, y
 
+    l1p = mxq.pack_l1t(l1t) if packed else None
+
     def run(q, u, y):
-        mxq.quantize(x, fmt_a, hadamard=had, l1t=l1t, u=u, out=q, workspace=ws)
+        if packed:
+            mxq.quantize(x, fmt_a, l1p=l1p, u=u, out=q, workspace=ws)
+        else:
+            mxq.quantize(x, fmt_a, hadamard=had, l1t=l1t, u=u, out=q, workspace=ws)
         mxq.gemm(q, qw, u=u, l2t=l2t, out=y)
 
     def snapshot(q, u, y):
