@@ -504,7 +504,6 @@ constexpr int kLrWaves = 8;
 
 template <int FMT, int NT, bool PK>
 __global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, LoraDownArgs lr) {
-  constexpr int U = NT <= 2 ? 2 : 1;   // groups in flight per wave
   __shared__ float part[kLrWaves][kLrRows][16 * NT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float g = tensor_scale<FMT>(p);
@@ -522,31 +521,23 @@ __global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, L
   v4f acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = v4f{};
-  for (int g0 = wave; g0 < groups; g0 += kLrWaves * U) {
-    uint4 xv[U][4], lv[U][NT][4];
+  // one group in flight per wave: loading the next group's operands ahead
+  // (two in flight) measured 6% slower on 4096 x 3072 at rank 32
+  for (int gi = wave; gi < groups; gi += kLrWaves) {
+    uint4 xv[4], lv[NT][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int gi = g0 + kLrWaves * u;
-      const bool ok = gi < groups;
+    for (int j = 0; j < 4; ++j) {
+      xv[j] = *reinterpret_cast<const uint4*>(xr + gi * 128 + 8 * j);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        xv[u][j] = ok ? *reinterpret_cast<const uint4*>(xr + gi * 128 + 8 * j) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          lv[u][t][j] = ok ? *reinterpret_cast<const uint4*>(
-                                 PK ? lp + (((int64_t)gi * NT + t) * 4 + j) * 512
-                                    : lp + (int64_t)t * 16 * lr.cols + gi * 128 + 8 * j)
-                           : make_uint4(0, 0, 0, 0);
-      }
+      for (int t = 0; t < NT; ++t)
+        lv[t][j] = *reinterpret_cast<const uint4*>(PK ? lp + (((int64_t)gi * NT + t) * 4 + j) * 512
+                                                      : lp + (int64_t)t * 16 * lr.cols + gi * 128 + 8 * j);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int gi = g0 + kLrWaves * u;
-      if (gi >= groups) break;
+    {
       float v[4][8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t w[4] = {xv[u][j].x, xv[u][j].y, xv[u][j].z, xv[u][j].w};
+        const uint32_t w[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           v[j][2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
@@ -605,10 +596,10 @@ __global__ __launch_bounds__(64 * kLrWaves) void quantize_lr_kernel(QParams p, L
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const v8bf af = __builtin_bit_cast(v8bf, xv[u][j]);
+        const v8bf af = __builtin_bit_cast(v8bf, xv[j]);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(v8bf, lv[u][t][j]),
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(v8bf, lv[t][j]),
                                                            acc[t], 0, 0, 0);
       }
     }
