@@ -163,8 +163,11 @@ typedef struct mxq_qtensor {
  *  workspace   device scratch of mxq_workspace_size(MXQ_OP_QUANTIZE, ...)
  *              bytes (only dynamic NVFP4 needs any).
  * Returns MXQ_ERR_SHAPE when cols is not a multiple of 32 (for NVFP4 too:
- * its 16-blocks are quantized in pairs) or of hadamard_n.  rows == 0 is a
- * no-op.
+ * its 16-blocks are quantized in pairs) or of hadamard_n.  rows == 0 or
+ * cols == 0 is a no-op: MXQ_OK once the checks that need no data have passed
+ * (dtype, out's format and sizes, hadamard_n, lr_rank's range, the column
+ * multiples); pointers, alignment, the workspace and the conditions of the
+ * low-rank path are checked for non-empty inputs only.
  */
 mxq_status mxq_quantize(const void* x, int32_t dtype, int64_t rows, int64_t cols,
                         int64_t ldx, int32_t hadamard_n,
@@ -194,7 +197,8 @@ mxq_status mxq_pack_l1t(const void* l1t, int32_t rank, int64_t cols, void* l1p, 
  * kilobytes.  It takes the fused quantize + projection path only: lr_rank a
  * multiple of 16 in [16, 128] (0 is MXQ_ERR_INVALID_ARG), bf16 x and
  * hadamard_n 0 (else MXQ_ERR_UNSUPPORTED), cols a multiple of 128 (else
- * MXQ_ERR_SHAPE).  Other arguments, workspace and errors as mxq_quantize.
+ * MXQ_ERR_SHAPE); like the other low-rank conditions these are checked for
+ * non-empty inputs.  Other arguments, workspace and errors as mxq_quantize.
  */
 mxq_status mxq_quantize_lrp(const void* x, int32_t dtype, int64_t rows, int64_t cols,
                             int64_t ldx, int32_t hadamard_n,

@@ -158,6 +158,11 @@ def test_validation_of_packed_lowrank_entry_points(lib):
     assert lrp(vp(16), 2, 4, 160, 160, 0, None, vp(32768), 32, u, 32, C.byref(q160), None, 0, None) == 4
     # missing u
     assert lrp(vp(16), 2, 4, 256, 256, 0, None, vp(32768), 32, None, 32, C.byref(q), None, 0, None) == 1
+    # an empty input is a no-op after the data-free checks: the low-rank
+    # conditions are not looked at, a rank outside [0, 128] still is
+    q0 = _lib.QTensorC(1, 0, 0, 256, vp(4096), 128, vp(8192), 8, None)
+    assert lrp(None, 2, 0, 256, 256, 0, None, None, 0, None, 32, C.byref(q0), None, 0, None) == 0
+    assert lrp(None, 2, 0, 256, 256, 0, None, None, 144, None, 32, C.byref(q0), None, 0, None) == 1
 
 
 def test_status_codes_and_no_device(lib):
