@@ -3,6 +3,8 @@ layer's shapes: the activation quantize reads bf16 (fp32) x once and writes
 codes (1/2 byte per element for 4-bit, 1 for FP8), one scale byte per block
 (32; 16 for NVFP4) and u in fp32; the GEMM does 2 M N K plus 2 M N r for a
 rank-r branch; each route is judged against its own dense MFMA peak."""
+import os
+
 import bench
 from fp8_quantized_linear_mxq_amd import workloads as wl
 
@@ -39,3 +41,15 @@ def test_gemm_flops_and_route_peaks():
     assert bench.route_peak_dtype("BF16", "INT4") == "bf16"
     assert bench.PEAK_TFLOPS["mxfp4"] == 10100.0 and bench.PEAK_TFLOPS["fp8"] == 5000.0
     assert bench.DEFAULT_WORKLOAD == "svdq_r32"
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says why,
+    before touching a device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
